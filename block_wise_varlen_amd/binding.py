@@ -1,0 +1,257 @@
+"""ctypes binding of libfcp.so: argument marshalling only.
+
+Every function has the name of the C entry point it wraps and does no arithmetic of
+its own: it checks dtypes and shapes, fills ``fcp_dims_t``, allocates outputs and the
+workspace with torch when the caller passes none, and passes device pointers and
+torch's current stream to the library. If libfcp.so is missing the import of any
+entry point raises; there is no fallback.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from .descriptors import PAIR_DTYPE, PAIR_FIELDS
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfcp.so")
+
+FCP_OK, FCP_ERR_INVALID_ARG, FCP_ERR_UNSUPPORTED, FCP_ERR_WORKSPACE, FCP_ERR_HIP, \
+    FCP_ERR_INTERNAL = range(6)
+FCP_OP_FWD, FCP_OP_MERGE, FCP_OP_BWD, FCP_OP_FWD_FUSED = range(4)
+
+# Every symbol include/fcp.h declares.
+SYMBOLS = ("fcp_abi_version", "fcp_status_string", "fcp_last_error", "fcp_validate",
+           "fcp_workspace_bytes", "fcp_block_attn_fwd", "fcp_merge_partials",
+           "fcp_block_attn_fwd_fused", "fcp_block_attn_bwd")
+
+
+class FcpError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("%s (%d): %s" % (_status_text(status), status, msg))
+        self.status = status
+
+
+class FcpPair(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int32) for f in PAIR_FIELDS]
+
+
+class FcpDims(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("q_rows", ctypes.c_int64), ("kv_rows", ctypes.c_int64),
+                ("part_rows", ctypes.c_int64)]
+
+
+assert ctypes.sizeof(FcpPair) == PAIR_DTYPE.itemsize == 32
+assert ctypes.sizeof(FcpDims) == 40
+
+_lib = None
+
+
+def load():
+    """Loads libfcp.so once; raises FileNotFoundError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise FileNotFoundError(
+            "libfcp.so not built at %s (run python -m block_wise_varlen_amd.build)" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    D = ctypes.POINTER(FcpDims)
+    sig = {
+        "fcp_abi_version": (ctypes.c_int, []),
+        "fcp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "fcp_last_error": (ctypes.c_char_p, []),
+        "fcp_validate": (ctypes.c_int, [D, P, I32, ctypes.c_int]),
+        "fcp_workspace_bytes": (SZ, [D, P, I32, ctypes.c_int]),
+        "fcp_block_attn_fwd": (ctypes.c_int, [D, P, P, P, P, I32, P, P, P, SZ, P]),
+        "fcp_merge_partials": (ctypes.c_int, [D, P, I32, P, P, P, P, P, SZ, P]),
+        "fcp_block_attn_fwd_fused": (ctypes.c_int, [D, P, P, P, P, I32, P, P, P, SZ, P]),
+        "fcp_block_attn_bwd": (ctypes.c_int, [D, P, P, P, P, P, P, P, I32, P, P, P, P, SZ,
+                                              P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    _lib = lib
+    return lib
+
+
+def _status_text(status):
+    try:
+        return load().fcp_status_string(status).decode()
+    except Exception:
+        return "status"
+
+
+def _check(status):
+    if status != FCP_OK:
+        raise FcpError(status, load().fcp_last_error().decode())
+
+
+def _pairs_arg(pairs):
+    arr = np.ascontiguousarray(np.asarray(pairs, dtype=PAIR_DTYPE))
+    return arr, arr.ctypes.data_as(ctypes.c_void_p), len(arr)
+
+
+def make_dims(num_q_heads, num_kv_heads, head_dim, q_rows, kv_rows, part_rows=0,
+              softmax_scale=0.0):
+    return FcpDims(num_q_heads, num_kv_heads, head_dim, float(softmax_scale), int(q_rows),
+                   int(kv_rows), int(part_rows))
+
+
+def _dims_from(q, k, part_rows=0, scale=0.0):
+    return make_dims(q.shape[1], k.shape[1], q.shape[2], q.shape[0], k.shape[0], part_rows,
+                     scale)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(t, stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_contiguous() \
+            or t.device.type != "cuda":
+        raise TypeError("%s must be a contiguous %s CUDA tensor" % (name, dtype))
+
+
+def _workspace(nbytes, like, ws):
+    """The caller's workspace as given (the library checks its size), or a new one."""
+    import torch
+    if ws is not None:
+        return ws, ws.numel() * ws.element_size()
+    if nbytes == 0:
+        return None, 0
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=like.device)
+    return ws, nbytes
+
+
+# ---- host-only entry points -------------------------------------------------------
+
+def fcp_abi_version():
+    return load().fcp_abi_version()
+
+
+def fcp_status_string(status):
+    return load().fcp_status_string(status).decode()
+
+
+def fcp_last_error():
+    return load().fcp_last_error().decode()
+
+
+def fcp_validate(dims, pairs, op):
+    arr, p, n = _pairs_arg(pairs)
+    return load().fcp_validate(ctypes.byref(dims), p, n, op)
+
+
+def fcp_workspace_bytes(dims, pairs, op):
+    arr, p, n = _pairs_arg(pairs)
+    return load().fcp_workspace_bytes(ctypes.byref(dims), p, n, op)
+
+
+# ---- device entry points ----------------------------------------------------------
+
+def fcp_block_attn_fwd(q, k, v, pairs, o_part=None, lse_part=None, part_rows=None,
+                       softmax_scale=0.0, ws=None, stream=None):
+    """Per-pair partials. Returns (o_part fp32 [part_rows, Hq, D], lse_part fp32)."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, n)
+    arr, p, n = _pairs_arg(pairs)
+    if part_rows is None:
+        part_rows = o_part.shape[0] if o_part is not None else \
+            int((arr["out_row"] + arr["q_len"]).max()) if n else 0
+    if o_part is None:
+        o_part = torch.empty((part_rows, q.shape[1], q.shape[2]), dtype=torch.float32,
+                             device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((part_rows, q.shape[1]), dtype=torch.float32, device=q.device)
+    _need(o_part, torch.float32, "o_part")
+    _need(lse_part, torch.float32, "lse_part")
+    dims = _dims_from(q, k, part_rows, softmax_scale)
+    lib = load()
+    ws, wsb = _workspace(lib.fcp_workspace_bytes(ctypes.byref(dims), p, n, FCP_OP_FWD), q, ws)
+    _check(lib.fcp_block_attn_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), p, n,
+                                  _ptr(o_part), _ptr(lse_part), _ptr(ws), wsb,
+                                  _stream(q, stream)))
+    return o_part, lse_part
+
+
+def fcp_merge_partials(pairs, o_part, lse_part, q_rows, num_kv_heads=1, o=None, lse=None,
+                       ws=None, stream=None):
+    """LSE merge into bf16 o [q_rows, Hq, D] and fp32 lse [q_rows, Hq]. Rows no pair
+    covers keep their previous contents (zeros when allocated here)."""
+    import torch
+    _need(o_part, torch.float32, "o_part")
+    _need(lse_part, torch.float32, "lse_part")
+    hq, d = o_part.shape[1], o_part.shape[2]
+    if o is None:
+        o = torch.zeros((q_rows, hq, d), dtype=torch.bfloat16, device=o_part.device)
+    if lse is None:
+        lse = torch.zeros((q_rows, hq), dtype=torch.float32, device=o_part.device)
+    _need(o, torch.bfloat16, "o")
+    _need(lse, torch.float32, "lse")
+    arr, p, n = _pairs_arg(pairs)
+    dims = make_dims(hq, num_kv_heads, d, q_rows, 0, o_part.shape[0])
+    lib = load()
+    wsn = lib.fcp_workspace_bytes(ctypes.byref(dims), p, n, FCP_OP_MERGE)
+    ws, wsb = _workspace(wsn, o_part, ws)
+    _check(lib.fcp_merge_partials(ctypes.byref(dims), p, n, _ptr(o_part), _ptr(lse_part),
+                                  _ptr(o), _ptr(lse), _ptr(ws), wsb, _stream(o_part, stream)))
+    return o, lse
+
+
+def fcp_block_attn_fwd_fused(q, k, v, pairs, o=None, lse=None, softmax_scale=0.0, ws=None,
+                             stream=None):
+    """Forward with the merge folded in: bf16 o [q_rows, Hq, D], fp32 lse [q_rows, Hq]."""
+    import torch
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, nm)
+    if o is None:
+        o = torch.zeros_like(q)
+    if lse is None:
+        lse = torch.zeros((q.shape[0], q.shape[1]), dtype=torch.float32, device=q.device)
+    _need(o, torch.bfloat16, "o")
+    _need(lse, torch.float32, "lse")
+    arr, p, n = _pairs_arg(pairs)
+    dims = _dims_from(q, k, 0, softmax_scale)
+    lib = load()
+    ws, wsb = _workspace(lib.fcp_workspace_bytes(ctypes.byref(dims), p, n, FCP_OP_FWD_FUSED),
+                         q, ws)
+    _check(lib.fcp_block_attn_fwd_fused(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), p, n,
+                                        _ptr(o), _ptr(lse), _ptr(ws), wsb, _stream(q, stream)))
+    return o, lse
+
+
+def fcp_block_attn_bwd(q, k, v, o, lse, dout, pairs, dq=None, dk=None, dv=None,
+                       softmax_scale=0.0, ws=None, stream=None):
+    """Adds gradients into fp32 dq, dk, dv (allocated zeroed here when not given)."""
+    import torch
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _need(t, torch.bfloat16, nm)
+    _need(lse, torch.float32, "lse")
+    if dq is None:
+        dq = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.zeros(k.shape, dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.zeros(v.shape, dtype=torch.float32, device=q.device)
+    for t, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need(t, torch.float32, nm)
+    arr, p, n = _pairs_arg(pairs)
+    dims = _dims_from(q, k, 0, softmax_scale)
+    lib = load()
+    ws, wsb = _workspace(lib.fcp_workspace_bytes(ctypes.byref(dims), p, n, FCP_OP_BWD), q, ws)
+    _check(lib.fcp_block_attn_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                  _ptr(lse), _ptr(dout), p, n, _ptr(dq), _ptr(dk), _ptr(dv),
+                                  _ptr(ws), wsb, _stream(q, stream)))
+    return dq, dk, dv

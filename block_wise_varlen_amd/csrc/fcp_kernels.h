@@ -1,0 +1,72 @@
+// Kernel argument blocks and launchers (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fcp_types.h"
+
+namespace fcp {
+
+struct FwdArgs {
+  const uint16_t* q;   // bf16 [q_rows, hq, D]
+  const uint16_t* k;   // bf16 [kv_rows, hkv, D]
+  const uint16_t* v;   // bf16 [kv_rows, hkv, D]
+  const QItem* items;  // n_items, in launch order
+  const KvSeg* segs;
+  int n_items;
+  int hq, hkv, group, hpw, n_hgroups;
+  float scale_log2;  // softmax scale * log2(e)
+  float* o_part;     // fp32 [part_rows, hq, D]   (per-pair mode)
+  float* lse_part;   // fp32 [part_rows, hq]
+  uint16_t* o;       // bf16 [q_rows, hq, D]      (final mode)
+  float* lse;        // fp32 [q_rows, hq]
+};
+
+struct MergeArgs {
+  const float* o_part;
+  const float* lse_part;
+  const RowItem* rows;
+  const int32_t* parts;  // out_row of each partial, grouped per Q range
+  int n_rows;
+  int hq;
+  uint16_t* o;  // bf16 [q_rows, hq, D]
+  float* lse;   // fp32 [q_rows, hq]
+};
+
+struct DeltaArgs {
+  const uint16_t* o;     // bf16 merged output
+  const uint16_t* dout;  // bf16 upstream gradient
+  const RowItem* rows;
+  int n_rows;
+  int hq;
+  float* delta;  // fp32 [q_rows, hq]
+};
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const float* lse;    // fp32 [q_rows, hq], natural log
+  const float* delta;  // fp32 [q_rows, hq]
+  const QItem* qitems;
+  const KvSeg* segs;
+  const KvItem* kvitems;
+  const QSeg* qsegs;
+  int n_qitems, n_kvitems;
+  int hq, hkv, group, hpw, n_hgroups;
+  float scale;       // softmax scale
+  float scale_log2;  // softmax scale * log2(e)
+  float* dq;         // fp32 [q_rows, hq, D]   (+=)
+  float* dk;         // fp32 [kv_rows, hkv, D] (+=)
+  float* dv;         // fp32 [kv_rows, hkv, D] (+=)
+};
+
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool final_out, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_delta(const DeltaArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t stream);
+
+}  // namespace fcp

@@ -1,0 +1,199 @@
+/*
+ * fcp.h -- C ABI of the block-level variable-length attention library for MI355X
+ * (gfx950). One worker's share of FCP-style context-parallel attention: fixed-size
+ * Q blocks attend to local or pulled KV blocks, every block pair yields a partial
+ * output with its log-sum-exp, and partials of the same query rows are combined by an
+ * associative LSE merge. A backward pass produces dQ, dK and dV.
+ *
+ * Sources. "Unleashing Scalable Context Parallelism for Foundation Models
+ * Pre-Training via FCP" (arXiv 2605.08524): Sec. 2.2 (attention over [H, L, D]
+ * tensors, causal and non-causal masks only, forward and backward both implemented,
+ * grouped-query attention so KV rather than Q moves between workers, per-slice
+ * results of one sequence reduce to the final output); Sec. 4.1 (fixed-size blocks,
+ * short sequences packed into blocks and computed through the kernel's
+ * variable-length interface); Sec. 4.2 (a worker computes pulled KV blocks with its
+ * local Q blocks one block, or c coalesced blocks, at a time). The attention formula
+ * itself is legible only on the paper's review page (xllm-io paper review of
+ * 2605.08524, section "核心公式与建模"): O = Softmax(QK^T / sqrt(D) (.) M) V; the mask
+ * M is read as excluding masked keys from the softmax.
+ *
+ * Conventions shared by every call
+ *  - Tensors are caller-owned device memory, token-major and contiguous:
+ *      q, dout, o        bf16  [q_rows,  num_q_heads,  head_dim]
+ *      k, v              bf16  [kv_rows, num_kv_heads, head_dim]
+ *      lse               fp32  [q_rows,  num_q_heads]      natural logarithm
+ *      o_part            fp32  [part_rows, num_q_heads, head_dim]
+ *      lse_part          fp32  [part_rows, num_q_heads]    natural logarithm
+ *      dq                fp32  [q_rows,  num_q_heads,  head_dim]
+ *      dk, dv            fp32  [kv_rows, num_kv_heads, head_dim]
+ *    bf16 is IEEE bfloat16 stored as 16-bit words.
+ *  - Query head h reads KV head h / (num_q_heads / num_kv_heads) (contiguous groups).
+ *  - `pairs` is HOST memory, read only during the call; it may be reused on return.
+ *  - `ws` is caller-owned device scratch of at least fcp_workspace_bytes(...) bytes for
+ *    the same op and arguments; it must stay untouched until the stream passes the
+ *    call. The library allocates no device memory; it owns only pinned host staging
+ *    buffers used to upload its work lists, reused once their copies complete.
+ *  - Calls enqueue work on `stream` and return without waiting for it. They may be
+ *    issued concurrently from several threads on distinct streams. Calls that share a
+ *    workspace or output buffers must be ordered by the caller.
+ *  - Return value: FCP_OK or an FCP_ERR_* code. No exception crosses the ABI and the
+ *    library prints nothing; fcp_last_error() gives a thread-local message. Device
+ *    faults surface at the caller's next synchronisation.
+ *  - n_pairs == 0 is a no-op that returns FCP_OK.
+ */
+#ifndef FCP_H_
+#define FCP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FCP_ABI_VERSION 1
+
+/* Status codes. */
+#define FCP_OK 0
+#define FCP_ERR_INVALID_ARG 1 /* null pointer, bad dims, pair out of range, overlap  */
+#define FCP_ERR_UNSUPPORTED 2 /* head_dim not 64/128, heads not grouped evenly, ... */
+#define FCP_ERR_WORKSPACE 3   /* ws missing or smaller than fcp_workspace_bytes()   */
+#define FCP_ERR_HIP 4         /* a HIP runtime call failed (text in last_error)     */
+#define FCP_ERR_INTERNAL 5    /* host-side failure inside the library (e.g. no memory) */
+
+/* Ops, for fcp_workspace_bytes() and fcp_validate(). */
+#define FCP_OP_FWD 0
+#define FCP_OP_MERGE 1
+#define FCP_OP_BWD 2
+#define FCP_OP_FWD_FUSED 3
+
+/* Pair flags. */
+#define FCP_PAIR_CAUSAL 1
+
+/*
+ * One block pair: the Q rows [q_start, q_start + q_len) of one sequence attend to the
+ * KV rows [kv_start, kv_start + kv_len) of the same sequence (FCP paper Sec. 2.2 and
+ * Sec. 4.2: a worker computes local Q blocks against local or pulled KV blocks; Sec.
+ * 4.1: a packed block holds several sequences, so one block pair may become several
+ * descriptors, one per same-sequence segment pair).
+ *   seq_id       informational; not used by the kernels.
+ *   q_start      first row in q / dout / o / lse / dq.            q_len  >= 1
+ *   kv_start     first row in k / v / dk / dv.                    kv_len >= 1
+ *   mask_offset  in-sequence position of Q row 0 minus that of KV row 0. With the
+ *                causal flag, key j (0-based within the pair) is visible to query i iff
+ *                j - i <= mask_offset; a query that sees no key of the pair gets an
+ *                empty partial (O = 0, LSE = -inf).
+ *   out_row      first row of this pair's partial in o_part / lse_part (fwd only).
+ *   flags        bit 0: causal. Other bits must be zero.
+ */
+typedef struct fcp_pair_t {
+  int32_t seq_id;
+  int32_t q_start;
+  int32_t q_len;
+  int32_t kv_start;
+  int32_t kv_len;
+  int32_t mask_offset;
+  int32_t out_row;
+  int32_t flags;
+} fcp_pair_t;
+
+/*
+ * Problem shape. num_q_heads must be a multiple of num_kv_heads, and the group size
+ * G = num_q_heads / num_kv_heads must be 1, 2, 4 or a multiple of 8. head_dim is 64
+ * or 128. softmax_scale 0 means 1/sqrt(head_dim) (the scale of the attention formula);
+ * otherwise it must be finite and positive. The row extents bound every pair.
+ */
+typedef struct fcp_dims_t {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  float softmax_scale;
+  int64_t q_rows;    /* rows of q, dout, o, lse, dq      */
+  int64_t kv_rows;   /* rows of k, v, dk, dv             */
+  int64_t part_rows; /* rows of o_part, lse_part (fwd, merge) */
+} fcp_dims_t;
+
+/* ABI version of the loaded library (FCP_ABI_VERSION at build time). */
+int fcp_abi_version(void);
+
+/* Static text for a status code. Never NULL. */
+const char* fcp_status_string(int status);
+
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* fcp_last_error(void);
+
+/*
+ * Host-only check of dims and pairs for `op` (no HIP call). Returns the status the
+ * corresponding entry point would return for these arguments before touching the GPU.
+ * FWD: pairs in range; partial-output ranges [out_row, out_row + q_len) disjoint.
+ * MERGE, BWD, FWD_FUSED: any two pairs' Q ranges are identical or disjoint.
+ * MERGE reads no K/V, so it does not check KV ranges against kv_rows.
+ */
+int fcp_validate(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t n_pairs, int op);
+
+/*
+ * Device workspace that `op` needs for these dims and pairs, in bytes (host-only).
+ * Returns 0 when the arguments are invalid (fcp_last_error() says why) or nothing is
+ * needed (n_pairs == 0).
+ */
+size_t fcp_workspace_bytes(const fcp_dims_t* dims, const fcp_pair_t* pairs,
+                           int32_t n_pairs, int op);
+
+/*
+ * Forward, one partial per pair (FCP paper Sec. 2.2: per-slice intermediate results).
+ * For every pair and query head, writes the pair's own normalised attention output
+ * over its visible keys to o_part rows [out_row, out_row + q_len) and its natural-log
+ * LSE to lse_part; queries with no visible key get O = 0 and LSE = -inf. Other rows of
+ * o_part / lse_part are left untouched. Arithmetic: bf16 products, fp32 accumulation
+ * and softmax.
+ */
+int fcp_block_attn_fwd(const fcp_dims_t* dims, const void* q, const void* k, const void* v,
+                       const fcp_pair_t* pairs, int32_t n_pairs, float* o_part,
+                       float* lse_part, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * LSE merge of partials (FCP paper Sec. 2.2: per-slice results reduce to the final
+ * output). Pairs with identical (q_start, q_len) form a group; for every row and head
+ * of a group, LSE = ln sum_i exp(LSE_i) and O = sum_i exp(LSE_i - LSE) O_i over the
+ * group's partials, written as bf16 `o` and fp32 `lse` at rows q_start... A row whose
+ * partials are all empty gets O = 0, LSE = -inf. Rows no pair covers are untouched.
+ * Partially overlapping Q ranges are an error.
+ */
+int fcp_merge_partials(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t n_pairs,
+                       const float* o_part, const float* lse_part, void* o, float* lse,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Forward with the merge folded in: for every group of pairs with identical Q range,
+ * one pass over all of the group's KV ranges writes the final bf16 O and fp32 LSE
+ * directly (same result as fcp_block_attn_fwd followed by fcp_merge_partials, without
+ * the fp32 partials; the execution side of the bottom-up coalescer, FCP paper Sec.
+ * 4.2). out_row is ignored. Partially overlapping Q ranges are an error.
+ */
+int fcp_block_attn_fwd_fused(const fcp_dims_t* dims, const void* q, const void* k,
+                             const void* v, const fcp_pair_t* pairs, int32_t n_pairs,
+                             void* o, float* lse, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/*
+ * Backward (FCP paper Sec. 2.2 states that a backward is implemented; the gradient
+ * here is the exact one of the forward). Takes the MERGED o (bf16) and lse (fp32) of
+ * the rows the pairs cover and the upstream gradient dout, and ADDS each pair's
+ * contribution to fp32 dq, dk and dv (the caller zeroes them first). With
+ * Delta_i = sum_d dout_i o_i, P_ij = exp(S_ij - lse_i) and dS_ij = P_ij (dP_ij - Delta_i):
+ * dv_j += sum_i P_ij dout_i, dk_j += scale sum_i dS_ij q_i, dq_i += scale sum_j dS_ij k_j,
+ * summed over the query heads of each KV head's group. Any two pairs' Q ranges must be
+ * identical or disjoint. Results are deterministic (no atomics).
+ */
+int fcp_block_attn_bwd(const fcp_dims_t* dims, const void* q, const void* k, const void* v,
+                       const void* o, const float* lse, const void* dout,
+                       const fcp_pair_t* pairs, int32_t n_pairs, float* dq, float* dk,
+                       float* dv, void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FCP_H_ */

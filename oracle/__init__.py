@@ -3,9 +3,9 @@
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py``
 may import this package. The product path (the HIP library and its binding) never
 does, and this package imports nothing from it. Parity status per function:
-  forward, partial, merge, backward, dq_rows: pinned (brute force, closed forms,
+  forward, partial, merge, backward, dq_rows, dkv_rows: pinned (brute force, closed forms,
   invariants, finite differences; see tests/test_oracle.py).
 """
-from .attention import SeqIndex, forward, partial, merge, backward, dq_rows
+from .attention import SeqIndex, forward, partial, merge, backward, dq_rows, dkv_rows
 
-__all__ = ["SeqIndex", "forward", "partial", "merge", "backward", "dq_rows"]
+__all__ = ["SeqIndex", "forward", "partial", "merge", "backward", "dq_rows", "dkv_rows"]

@@ -219,3 +219,47 @@ def dq_rows(qf, kf, vf, dof, idx, rows, scale=None):
                 ds = p * (dout @ vv.T - delta[:, None])
                 out[c, h] = (ds @ kk) * sc
     return out
+
+
+def dkv_rows(qf, kf, vf, dof, idx, kv_rows, scale=None):
+    """dK and dV for the given KV rows only: each key's gradient sums over the owned
+    queries of its sequence that see it, and each such query needs its own full forward
+    (LSE, O, Delta). Returns (dK, dV), each [len(kv_rows), Hkv, D]."""
+    kv_rows = np.asarray(kv_rows, dtype=np.int64)
+    group = idx.hq // idx.hkv
+    sc = _scale(idx.d, scale)
+    dk = np.zeros((len(kv_rows), idx.hkv, idx.d))
+    dv = np.zeros((len(kv_rows), idx.hkv, idx.d))
+    pos_of = {}
+    for s, m in idx.kv_row_of_pos.items():
+        for p in np.nonzero(m >= 0)[0]:
+            pos_of[int(m[p])] = (s, int(p))
+    rows = idx.owned_rows()
+    for ki, kr in enumerate(kv_rows):
+        s, kp = pos_of[int(kr)]
+        qsel = rows[(idx.q_row_seq[rows] == s) &
+                    ((idx.q_row_pos[rows] >= kp) if idx.causal else True)]
+        if len(qsel) == 0:
+            continue
+        pos = idx.q_row_pos[qsel]
+        krows = idx.visible_key_rows(s, pos.max())
+        kpos = np.arange(len(krows))
+        step = _chunk(len(krows))
+        for a in range(0, len(qsel), step):
+            rc, qp = qsel[a:a + step], pos[a:a + step]
+            mask = (kpos[None, :] <= qp[:, None]) if idx.causal else None
+            for h in range(idx.hq):
+                g = h // group
+                kk, vv = kf[krows, g], vf[krows, g]
+                smat = (qf[rc, h] @ kk.T) * sc
+                if mask is not None:
+                    smat = np.where(mask, smat, -np.inf)
+                m = smat.max(axis=1, keepdims=True)
+                lse = m[:, 0] + np.log(np.exp(smat - m).sum(axis=1))
+                p = np.exp(smat[:, kp] - lse)
+                dout = dof[rc, h]
+                delta = (dout * (np.exp(smat - lse[:, None]) @ vv)).sum(axis=1)
+                ds = p * (dout @ vf[kr, g] - delta)
+                dk[ki, g] += (ds @ qf[rc, h]) * sc
+                dv[ki, g] += p @ dout
+    return dk, dv

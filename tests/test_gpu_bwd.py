@@ -1,0 +1,118 @@
+"""GPU parity of the backward (dQ, dK, dV) against the float64 oracle, through the C ABI.
+
+Gate per gradient tensor (the pages give none; the arithmetic is bf16 products with fp32
+accumulation, and the GPU's Delta uses the bf16-stored merged O): relative L2 <= 1e-2 and
+max-abs <= 5e-2 * max|reference|.
+"""
+import numpy as np
+import pytest
+
+import fcp_workloads as W
+import oracle
+from block_wise_varlen_amd import binding as B
+from block_wise_varlen_amd.descriptors import build_pairs
+from tests import gpu_util as U
+from tests.test_gpu_fwd import SMALL
+
+pytestmark = pytest.mark.gpu
+
+G_REL_L2 = 1e-2
+G_MAX_REL = 5e-2
+
+
+def check_grad(got, ref, what):
+    got = np.asarray(got, dtype=np.float64)
+    assert not np.isnan(got).any(), "%s: NaN" % what
+    scale = max(np.abs(ref).max(), 1e-30)
+    err = np.abs(got - ref).max()
+    assert err <= G_MAX_REL * scale, "%s: max-abs %.3g vs max|ref| %.3g" % (what, err, scale)
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+    assert rel <= G_REL_L2, "%s: rel-L2 %.3g" % (what, rel)
+
+
+def _fwd_bwd(wl, dev, pairs):
+    o, lse = B.fcp_block_attn_fwd_fused(dev["q"], dev["k"], dev["v"], pairs)
+    dq, dk, dv = B.fcp_block_attn_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], pairs)
+    return o, lse, dq, dk, dv
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_backward_matches_oracle(gpu, name):
+    import torch
+    wl = SMALL[name]()
+    dev, x = U.inputs(wl, seed=5)
+    pairs = build_pairs(wl)
+    _, _, dq, dk, dv = _fwd_bwd(wl, dev, pairs)
+    torch.cuda.synchronize()
+    idx = oracle.SeqIndex(wl)
+    rq, rk, rv = oracle.backward(x["q"], x["k"], x["v"], x["do"], idx)
+    rows = idx.owned_rows()
+    check_grad(dq.cpu().numpy()[rows], rq[rows], name + " dQ")
+    check_grad(dk.cpu().numpy(), rk, name + " dK")
+    check_grad(dv.cpu().numpy(), rv, name + " dV")
+
+
+def test_backward_accumulates_and_is_deterministic(gpu):
+    """Outputs are added to (+=); two runs give bitwise-equal results (no atomics)."""
+    import torch
+    wl = SMALL["g4-d128-ffd-coalesce"]()
+    dev, _ = U.inputs(wl, seed=6)
+    pairs = build_pairs(wl)
+    o, lse, dq, dk, dv = _fwd_bwd(wl, dev, pairs)
+    dq2, dk2, dv2 = B.fcp_block_attn_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"],
+                                         pairs)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    B.fcp_block_attn_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], pairs, dq=dq2,
+                         dk=dk2, dv=dv2)
+    torch.cuda.synchronize()
+    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        torch.testing.assert_close(b, 2 * a, rtol=1e-6, atol=1e-6)
+
+
+def _key_sample(wl):
+    rows = []
+    for s, length in enumerate(wl.seqlens):
+        for p in (length - 1, length - 17, length // 2 if length <= 4096 else length - 200):
+            for seg in wl.kv_segments():
+                if seg.seq == s and seg.pos0 <= p < seg.pos0 + seg.length:
+                    rows.append(seg.row0 + p - seg.pos0)
+    return np.array(sorted(set(rows)), dtype=np.int64)
+
+
+@pytest.mark.parametrize("cfg", ["config2", "config3-1024", "config3-4096-nc"])
+def test_full_size_sampled(gpu, cfg):
+    import torch
+    wl = {"config2": lambda: W.config2(0),
+          "config3-1024": lambda: W.config3(1024, True),
+          "config3-4096-nc": lambda: W.config3(4096, False)}[cfg]()
+    dev, x = U.inputs(wl, seed=0)
+    pairs = build_pairs(wl)
+    _, _, dq, dk, dv = _fwd_bwd(wl, dev, pairs)
+    torch.cuda.synchronize()
+    idx = oracle.SeqIndex(wl)
+    rows = U.sample_rows(wl, 24)
+    rq = oracle.dq_rows(x["q"], x["k"], x["v"], x["do"], idx, rows)
+    check_grad(dq.index_select(0, torch.as_tensor(rows, device=dq.device)).cpu().numpy(), rq,
+               cfg + " dQ rows")
+    if wl.causal:
+        # Keys near the end of each sequence are seen by few queries, so the oracle can
+        # afford them. (Under the non-causal mask every query sees every key, which puts
+        # a per-key oracle out of reach at 32K; the dV sum below covers all keys.)
+        krows = _key_sample(wl)
+        rk, rv = oracle.dkv_rows(x["q"], x["k"], x["v"], x["do"], idx, krows)
+        kidx = torch.as_tensor(krows, device=dk.device)
+        check_grad(dk.index_select(0, kidx).cpu().numpy(), rk, cfg + " dK keys")
+        check_grad(dv.index_select(0, kidx).cpu().numpy(), rv, cfg + " dV keys")
+    # Rows of P sum to one: per sequence and KV head, sum_j dV_j = sum over the group's
+    # query heads and the sequence's owned queries of dO.
+    g = wl.num_q_heads // wl.num_kv_heads
+    dv_h = dv.cpu().numpy()
+    do_h = x["do"]
+    for s in range(len(wl.seqlens)):
+        kr = idx.kv_row_of_pos[s]
+        qr = np.nonzero(idx.q_row_seq == s)[0]
+        lhs = dv_h[kr].sum(axis=0)
+        rhs = do_h[qr].reshape(len(qr), wl.num_kv_heads, g, -1).sum(axis=(0, 2))
+        rel = np.linalg.norm(lhs - rhs) / np.linalg.norm(rhs)
+        assert rel < 2e-2, (s, rel)

@@ -1,0 +1,137 @@
+"""GPU parity of the forward path (per-pair partials, LSE merge, fused forward) against
+the float64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+import fcp_workloads as W
+import oracle
+from block_wise_varlen_amd import binding as B
+from block_wise_varlen_amd.descriptors import build_pairs, part_rows
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "config1": lambda: W.config1(),
+    "config1-noncausal": lambda: W.config1(causal=False),
+    "config1-split3": lambda: W.config1(kv_split=3),
+    "g8-d128-ragged": lambda: W.custom([300, 128, 596], 256, 8, 1, 128, True, kv_split=2),
+    "g2-d64-noncausal": lambda: W.custom([77, 1, 200, 33], 64, 4, 2, 64, False),
+    "g16-d128": lambda: W.custom([150, 90, 3], 128, 16, 1, 128, True, kv_split=2),
+    "g1-d128": lambda: W.custom([129, 64, 65], 64, 2, 2, 128, True),
+    "g4-d128-ffd-coalesce": lambda: W.custom([700, 45, 333, 9], 128, 8, 2, 128, True,
+                                             shard="ffd", coalesce=3),
+    "zigzag-small": lambda: W.custom([2048], 128, 8, 1, 128, True, q_ids=[1, 14],
+                                     kv_ids=list(range(15)), coalesce=4),
+}
+
+
+def _run_partials(wl, dev, pairs):
+    o_part, lse_part = B.fcp_block_attn_fwd(dev["q"], dev["k"], dev["v"], pairs,
+                                            part_rows=part_rows(pairs))
+    return o_part, lse_part
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_partials_match_oracle(gpu, name):
+    wl = SMALL[name]()
+    dev, x = U.inputs(wl, seed=1)
+    pairs = build_pairs(wl)
+    o_part, lse_part = _run_partials(wl, dev, pairs)
+    o_part, lse_part = o_part.cpu().numpy(), lse_part.cpu().numpy()
+    idx = oracle.SeqIndex(wl)
+    kpos = U.kv_row_pos(wl)
+    for i, p in enumerate(pairs):
+        qr = np.arange(p["q_start"], p["q_start"] + p["q_len"])
+        kr = np.arange(p["kv_start"], p["kv_start"] + p["kv_len"])
+        o_ref, l_ref = oracle.partial(x["q"], x["k"], x["v"], qr, idx.q_row_pos[qr], kr,
+                                      kpos[kr], wl.causal, wl.num_q_heads, wl.num_kv_heads)
+        sl = slice(p["out_row"], p["out_row"] + p["q_len"])
+        U.check_attn(o_part[sl], lse_part[sl], o_ref, l_ref, "%s pair %d" % (name, i))
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_merge_and_fused_match_oracle(gpu, name):
+    import torch
+    wl = SMALL[name]()
+    dev, x = U.inputs(wl, seed=2)
+    pairs = build_pairs(wl)
+    o_part, lse_part = _run_partials(wl, dev, pairs)
+    o, lse = B.fcp_merge_partials(pairs, o_part, lse_part, wl.q_rows, wl.num_kv_heads)
+    of, lf = B.fcp_block_attn_fwd_fused(dev["q"], dev["k"], dev["v"], pairs)
+    torch.cuda.synchronize()
+    idx = oracle.SeqIndex(wl)
+    rows = idx.owned_rows()
+    o_ref, l_ref = oracle.forward(x["q"], x["k"], x["v"], idx)
+    U.check_attn(U.bf16_to_f64(o)[rows], lse.cpu().numpy()[rows], o_ref, l_ref, name + " merge")
+    U.check_attn(U.bf16_to_f64(of)[rows], lf.cpu().numpy()[rows], o_ref, l_ref, name + " fused")
+
+
+def test_softmax_scale_and_constant_v(gpu):
+    import torch
+    wl = W.custom([100, 37], 64, 8, 1, 128, True)
+    dev, x = U.inputs(wl, seed=3)
+    pairs = build_pairs(wl)
+    o, lse = B.fcp_block_attn_fwd_fused(dev["q"], dev["k"], dev["v"], pairs, softmax_scale=0.21)
+    idx = oracle.SeqIndex(wl)
+    o_ref, l_ref = oracle.forward(x["q"], x["k"], x["v"], idx, scale=0.21)
+    U.check_attn(U.bf16_to_f64(o), lse.cpu().numpy(), o_ref, l_ref, "scale 0.21")
+    vc = torch.full_like(dev["v"], 0.8125)   # exactly representable in bf16
+    oc, _ = B.fcp_block_attn_fwd_fused(dev["q"], dev["k"], vc, pairs)
+    assert np.abs(U.bf16_to_f64(oc) - 0.8125).max() <= 4e-3
+
+
+def test_forward_is_deterministic(gpu):
+    import torch
+    wl = W.custom([700, 45, 333, 9], 128, 8, 2, 128, True, shard="ffd", kv_split=2)
+    dev, _ = U.inputs(wl, seed=4, which=("q", "k", "v"))
+    pairs = build_pairs(wl)
+    a = _run_partials(wl, dev, pairs)
+    b = _run_partials(wl, dev, pairs)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("cfg", ["config2", "config3-512", "config3-4096", "config3-1024-nc"])
+def test_full_size_sampled(gpu, cfg):
+    """The bench's launch configuration at full size, checked on sampled rows."""
+    import torch
+    wl = {"config2": lambda: W.config2(0),
+          "config3-512": lambda: W.config3(512, True),
+          "config3-4096": lambda: W.config3(4096, True),
+          "config3-1024-nc": lambda: W.config3(1024, False)}[cfg]()
+    dev, x = U.inputs(wl, seed=0, which=("q", "k", "v"))
+    pairs = build_pairs(wl)
+    o_part, lse_part = _run_partials(wl, dev, pairs)
+    o, lse = B.fcp_merge_partials(pairs, o_part, lse_part, wl.q_rows, wl.num_kv_heads)
+    del o_part, lse_part
+    of, lf = B.fcp_block_attn_fwd_fused(dev["q"], dev["k"], dev["v"], pairs)
+    torch.cuda.synchronize()
+    rows = U.sample_rows(wl, 48)
+    idx = oracle.SeqIndex(wl)
+    o_ref, l_ref = oracle.forward(x["q"], x["k"], x["v"], idx, rows=rows)
+    ridx = torch.as_tensor(rows, device=o.device)
+    U.check_attn(U.bf16_to_f64(o.index_select(0, ridx)), lse.index_select(0, ridx).cpu().numpy(),
+                 o_ref, l_ref, cfg + " merge")
+    U.check_attn(U.bf16_to_f64(of.index_select(0, ridx)),
+                 lf.index_select(0, ridx).cpu().numpy(), o_ref, l_ref, cfg + " fused")
+
+
+def test_error_paths_do_not_launch(gpu):
+    import torch
+    wl = W.config1()
+    dev, _ = U.inputs(wl, seed=0, which=("q", "k", "v"))
+    pairs = build_pairs(wl)
+    bad = pairs.copy()
+    bad["kv_len"][0] = 10 ** 6
+    with pytest.raises(B.FcpError) as e:
+        B.fcp_block_attn_fwd(dev["q"], dev["k"], dev["v"], bad, part_rows=part_rows(pairs))
+    assert e.value.status == B.FCP_ERR_INVALID_ARG
+    # undersized workspace
+    dims = B.make_dims(4, 1, 64, wl.q_rows, wl.kv_rows, part_rows(pairs))
+    need = B.fcp_workspace_bytes(dims, pairs, B.FCP_OP_FWD)
+    ws = torch.empty(need - 256, dtype=torch.uint8, device=gpu)
+    with pytest.raises(B.FcpError) as e:
+        B.fcp_block_attn_fwd(dev["q"], dev["k"], dev["v"], pairs, part_rows=part_rows(pairs),
+                             ws=ws)
+    assert e.value.status == B.FCP_ERR_WORKSPACE

@@ -280,3 +280,15 @@ def test_dq_rows_matches_full_backward():
     rows = np.array([0, 3, 10, 22, 26])
     np.testing.assert_allclose(oracle.dq_rows(x["q"], x["k"], x["v"], x["do"], idx, rows),
                                dq[rows], atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_dkv_rows_matches_full_backward(causal):
+    wl = W.custom([9, 14, 4], 5, 4, 2, 8, causal)
+    x = _inputs(wl)
+    idx = oracle.SeqIndex(wl)
+    _, dk, dv = oracle.backward(x["q"], x["k"], x["v"], x["do"], idx)
+    rows = np.array([0, 4, 8, 9, 15, 22, 23, 26])
+    sk, sv = oracle.dkv_rows(x["q"], x["k"], x["v"], x["do"], idx, rows)
+    np.testing.assert_allclose(sk, dk[rows], atol=1e-13)
+    np.testing.assert_allclose(sv, dv[rows], atol=1e-13)
