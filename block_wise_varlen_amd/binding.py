@@ -22,7 +22,9 @@ FCP_OP_FWD, FCP_OP_MERGE, FCP_OP_BWD, FCP_OP_FWD_FUSED = range(4)
 # Every symbol include/fcp.h declares.
 SYMBOLS = ("fcp_abi_version", "fcp_status_string", "fcp_last_error", "fcp_validate",
            "fcp_workspace_bytes", "fcp_block_attn_fwd", "fcp_merge_partials",
-           "fcp_block_attn_fwd_fused", "fcp_block_attn_bwd")
+           "fcp_block_attn_fwd_fused", "fcp_block_attn_bwd", "fcp_timing_enable",
+           "fcp_timing_read", "fcp_kernel_name")
+FCP_KERNEL_COUNT = 6
 
 
 class FcpError(RuntimeError):
@@ -70,6 +72,9 @@ def load():
         "fcp_block_attn_fwd_fused": (ctypes.c_int, [D, P, P, P, P, I32, P, P, P, SZ, P]),
         "fcp_block_attn_bwd": (ctypes.c_int, [D, P, P, P, P, P, P, P, I32, P, P, P, P, SZ,
                                               P]),
+        "fcp_timing_enable": (ctypes.c_int, [ctypes.c_int]),
+        "fcp_timing_read": (ctypes.c_int, [P, P, I32]),
+        "fcp_kernel_name": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -123,11 +128,13 @@ def _need(t, dtype, name):
         raise TypeError("%s must be a contiguous %s CUDA tensor" % (name, dtype))
 
 
-def _workspace(nbytes, like, ws):
-    """The caller's workspace as given (the library checks its size), or a new one."""
+def _workspace(size_fn, like, ws):
+    """The caller's workspace as given (the library checks its size), or a new one of
+    size_fn() bytes."""
     import torch
     if ws is not None:
         return ws, ws.numel() * ws.element_size()
+    nbytes = size_fn()
     if nbytes == 0:
         return None, 0
     ws = torch.empty(nbytes, dtype=torch.uint8, device=like.device)
@@ -179,7 +186,8 @@ def fcp_block_attn_fwd(q, k, v, pairs, o_part=None, lse_part=None, part_rows=Non
     _need(lse_part, torch.float32, "lse_part")
     dims = _dims_from(q, k, part_rows, softmax_scale)
     lib = load()
-    ws, wsb = _workspace(lib.fcp_workspace_bytes(ctypes.byref(dims), p, n, FCP_OP_FWD), q, ws)
+    ws, wsb = _workspace(lambda: lib.fcp_workspace_bytes(ctypes.byref(dims), p, n, FCP_OP_FWD),
+                         q, ws)
     _check(lib.fcp_block_attn_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), p, n,
                                   _ptr(o_part), _ptr(lse_part), _ptr(ws), wsb,
                                   _stream(q, stream)))
@@ -203,8 +211,8 @@ def fcp_merge_partials(pairs, o_part, lse_part, q_rows, num_kv_heads=1, o=None, 
     arr, p, n = _pairs_arg(pairs)
     dims = make_dims(hq, num_kv_heads, d, q_rows, 0, o_part.shape[0])
     lib = load()
-    wsn = lib.fcp_workspace_bytes(ctypes.byref(dims), p, n, FCP_OP_MERGE)
-    ws, wsb = _workspace(wsn, o_part, ws)
+    ws, wsb = _workspace(
+        lambda: lib.fcp_workspace_bytes(ctypes.byref(dims), p, n, FCP_OP_MERGE), o_part, ws)
     _check(lib.fcp_merge_partials(ctypes.byref(dims), p, n, _ptr(o_part), _ptr(lse_part),
                                   _ptr(o), _ptr(lse), _ptr(ws), wsb, _stream(o_part, stream)))
     return o, lse
@@ -225,8 +233,8 @@ def fcp_block_attn_fwd_fused(q, k, v, pairs, o=None, lse=None, softmax_scale=0.0
     arr, p, n = _pairs_arg(pairs)
     dims = _dims_from(q, k, 0, softmax_scale)
     lib = load()
-    ws, wsb = _workspace(lib.fcp_workspace_bytes(ctypes.byref(dims), p, n, FCP_OP_FWD_FUSED),
-                         q, ws)
+    ws, wsb = _workspace(
+        lambda: lib.fcp_workspace_bytes(ctypes.byref(dims), p, n, FCP_OP_FWD_FUSED), q, ws)
     _check(lib.fcp_block_attn_fwd_fused(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), p, n,
                                         _ptr(o), _ptr(lse), _ptr(ws), wsb, _stream(q, stream)))
     return o, lse
@@ -250,8 +258,28 @@ def fcp_block_attn_bwd(q, k, v, o, lse, dout, pairs, dq=None, dk=None, dv=None,
     arr, p, n = _pairs_arg(pairs)
     dims = _dims_from(q, k, 0, softmax_scale)
     lib = load()
-    ws, wsb = _workspace(lib.fcp_workspace_bytes(ctypes.byref(dims), p, n, FCP_OP_BWD), q, ws)
+    ws, wsb = _workspace(lambda: lib.fcp_workspace_bytes(ctypes.byref(dims), p, n, FCP_OP_BWD),
+                         q, ws)
     _check(lib.fcp_block_attn_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                   _ptr(lse), _ptr(dout), p, n, _ptr(dq), _ptr(dk), _ptr(dv),
                                   _ptr(ws), wsb, _stream(q, stream)))
     return dq, dk, dv
+
+
+# ---- per-kernel timing ------------------------------------------------------------
+
+def fcp_timing_enable(on=True):
+    _check(load().fcp_timing_enable(1 if on else 0))
+
+
+def fcp_kernel_name(kid):
+    return load().fcp_kernel_name(kid).decode()
+
+
+def fcp_timing_read():
+    """{kernel name: (total ms, launches)} since the last read (waits for the events)."""
+    tot = (ctypes.c_double * FCP_KERNEL_COUNT)()
+    cnt = (ctypes.c_int32 * FCP_KERNEL_COUNT)()
+    _check(load().fcp_timing_read(ctypes.cast(tot, ctypes.c_void_p),
+                                  ctypes.cast(cnt, ctypes.c_void_p), FCP_KERNEL_COUNT))
+    return {fcp_kernel_name(i): (tot[i], cnt[i]) for i in range(FCP_KERNEL_COUNT) if cnt[i]}

@@ -93,6 +93,49 @@ int check_device() {
   return FCP_OK;
 }
 
+// Optional per-kernel timing: event pairs recorded around launches while enabled.
+struct TimedLaunch {
+  int id;
+  hipEvent_t begin, end;
+};
+std::mutex g_time_mu;
+bool g_time_on = false;
+std::vector<TimedLaunch> g_time_pending;
+std::vector<hipEvent_t> g_time_free;
+
+hipEvent_t take_event() {
+  if (!g_time_free.empty()) {
+    hipEvent_t e = g_time_free.back();
+    g_time_free.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` (which enqueues one kernel on `stream`), bracketed by events if timing
+// is on.
+template <class F>
+hipError_t timed(int id, hipStream_t stream, F&& launch) {
+  hipEvent_t b = nullptr, e = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_time_mu);
+    if (g_time_on) {
+      b = take_event();
+      e = take_event();
+    }
+  }
+  if (b && e) hipEventRecord(b, stream);
+  const hipError_t err = launch();
+  if (b && e) {
+    hipEventRecord(e, stream);
+    std::lock_guard<std::mutex> lk(g_time_mu);
+    g_time_pending.push_back(TimedLaunch{id, b, e});
+  }
+  return err;
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int need_ptrs(std::initializer_list<const void*> ptrs) {
@@ -158,6 +201,50 @@ const char* fcp_status_string(int status) {
 
 const char* fcp_last_error(void) { return g_err.c_str(); }
 
+int fcp_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_time_mu);
+  g_time_on = on != 0;
+  return FCP_OK;
+}
+
+int fcp_timing_read(double* total_ms, int32_t* launches, int32_t n) {
+  return guarded([&] {
+    std::vector<TimedLaunch> recs;
+    {
+      std::lock_guard<std::mutex> lk(g_time_mu);
+      recs.swap(g_time_pending);
+    }
+    for (int32_t i = 0; i < n; ++i) {
+      if (total_ms) total_ms[i] = 0.0;
+      if (launches) launches[i] = 0;
+    }
+    int st = FCP_OK;
+    for (const TimedLaunch& r : recs) {
+      float ms = 0.f;
+      hipError_t e = hipEventSynchronize(r.end);
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.begin, r.end);
+      if (e != hipSuccess) {
+        st = hip_err(e, "timing event");
+      } else if (r.id < n) {
+        if (total_ms) total_ms[r.id] += ms;
+        if (launches) launches[r.id] += 1;
+      }
+    }
+    std::lock_guard<std::mutex> lk(g_time_mu);
+    for (const TimedLaunch& r : recs) {
+      g_time_free.push_back(r.begin);
+      g_time_free.push_back(r.end);
+    }
+    return st;
+  });
+}
+
+const char* fcp_kernel_name(int id) {
+  static const char* names[FCP_KERNEL_COUNT] = {"fwd_partial", "fwd_fused", "merge",
+                                                "bwd_delta",   "bwd_dq",    "bwd_dkdv"};
+  return (id >= 0 && id < FCP_KERNEL_COUNT) ? names[id] : "";
+}
+
 int fcp_validate(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t n_pairs, int op) {
   return guarded([&] {
     std::string msg;
@@ -200,7 +287,8 @@ int fcp_block_attn_fwd(const fcp_dims_t* dims, const void* q, const void* k, con
     a.scale_log2 = s.scale * 1.4426950408889634f;
     a.o_part = o_part;
     a.lse_part = lse_part;
-    const hipError_t e = fcp::launch_fwd(a, s.d, false, stream);
+    const hipError_t e =
+        timed(FCP_KERNEL_FWD, stream, [&] { return fcp::launch_fwd(a, s.d, false, stream); });
     return e == hipSuccess ? FCP_OK : hip_err(e, "forward launch");
   });
 }
@@ -225,7 +313,8 @@ int fcp_block_attn_fwd_fused(const fcp_dims_t* dims, const void* q, const void* 
     a.scale_log2 = s.scale * 1.4426950408889634f;
     a.o = static_cast<uint16_t*>(o);
     a.lse = lse;
-    const hipError_t e = fcp::launch_fwd(a, s.d, true, stream);
+    const hipError_t e = timed(FCP_KERNEL_FWD_FUSED, stream,
+                                [&] { return fcp::launch_fwd(a, s.d, true, stream); });
     return e == hipSuccess ? FCP_OK : hip_err(e, "fused forward launch");
   });
 }
@@ -247,7 +336,8 @@ int fcp_merge_partials(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t 
     a.hq = P.shape.hq;
     a.o = static_cast<uint16_t*>(o);
     a.lse = lse;
-    const hipError_t e = fcp::launch_merge(a, P.shape.d, stream);
+    const hipError_t e =
+        timed(FCP_KERNEL_MERGE, stream, [&] { return fcp::launch_merge(a, P.shape.d, stream); });
     return e == hipSuccess ? FCP_OK : hip_err(e, "merge launch");
   });
 }
@@ -270,7 +360,8 @@ int fcp_block_attn_bwd(const fcp_dims_t* dims, const void* q, const void* k, con
     da.n_rows = P.n_rows;
     da.hq = s.hq;
     da.delta = delta;
-    hipError_t e = fcp::launch_delta(da, s.d, stream);
+    hipError_t e =
+        timed(FCP_KERNEL_DELTA, stream, [&] { return fcp::launch_delta(da, s.d, stream); });
     if (e != hipSuccess) return hip_err(e, "delta launch");
     fcp::BwdArgs a{};
     a.q = static_cast<const uint16_t*>(q);
@@ -291,9 +382,9 @@ int fcp_block_attn_bwd(const fcp_dims_t* dims, const void* q, const void* k, con
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
-    e = fcp::launch_bwd_dq(a, s.d, stream);
+    e = timed(FCP_KERNEL_DQ, stream, [&] { return fcp::launch_bwd_dq(a, s.d, stream); });
     if (e != hipSuccess) return hip_err(e, "dQ launch");
-    e = fcp::launch_bwd_dkdv(a, s.d, stream);
+    e = timed(FCP_KERNEL_DKDV, stream, [&] { return fcp::launch_bwd_dkdv(a, s.d, stream); });
     if (e != hipSuccess) return hip_err(e, "dK/dV launch");
     return FCP_OK;
   });

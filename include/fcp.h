@@ -192,6 +192,29 @@ int fcp_block_attn_bwd(const fcp_dims_t* dims, const void* q, const void* k, con
                        const fcp_pair_t* pairs, int32_t n_pairs, float* dq, float* dk,
                        float* dv, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Optional per-kernel timing, for measurement tools (not needed for computing).
+ * Kernel ids: FCP_KERNEL_FWD (per-pair forward), FCP_KERNEL_FWD_FUSED, FCP_KERNEL_MERGE,
+ * FCP_KERNEL_DELTA (backward preprocessing), FCP_KERNEL_DQ, FCP_KERNEL_DKDV.
+ * fcp_timing_enable(1): from now on every kernel launch, from any thread, is bracketed by
+ * a pair of HIP events recorded on the call's stream. fcp_timing_enable(0) stops that.
+ * fcp_timing_read(): waits for every recorded pair, adds each pair's elapsed time to
+ * total_ms[id] and 1 to launches[id] for id < n (arrays of n >= FCP_KERNEL_COUNT entries,
+ * zeroed by the call first), then forgets the pairs. Returns FCP_OK or FCP_ERR_HIP.
+ * fcp_kernel_name(id) gives the kernel's name ("" for an unknown id).
+ */
+#define FCP_KERNEL_FWD 0
+#define FCP_KERNEL_FWD_FUSED 1
+#define FCP_KERNEL_MERGE 2
+#define FCP_KERNEL_DELTA 3
+#define FCP_KERNEL_DQ 4
+#define FCP_KERNEL_DKDV 5
+#define FCP_KERNEL_COUNT 6
+
+int fcp_timing_enable(int on);
+int fcp_timing_read(double* total_ms, int32_t* launches, int32_t n);
+const char* fcp_kernel_name(int id);
+
 #ifdef __cplusplus
 }
 #endif
