@@ -59,25 +59,87 @@ __device__ __forceinline__ u16 f32_to_bf16(float x) {
   return __builtin_bit_cast(u16, b);
 }
 
-// Low halves (element 2w) or high halves (element 2w + 1) of two dwords, packed
-// lo | hi << 16 (v_perm_b32).
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
-}
-
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
-// Position of key k inside a transposed tile row, such that the eight keys one lane
-// half feeds to a 32x32x16 MFMA (result-layout rows 8*(s/4) + 4*half + s%4 of a 16-key
-// chunk, slot s = 0..7) are contiguous: within each 16-key chunk the 4-key groups 1 and
-// 2 trade places.
-__device__ __forceinline__ int tpos(int k) {
-  const int g = (k >> 2) & 3;
-  const int pg = (g == 1) ? 2 : (g == 2 ? 1 : g);
-  return (k & ~15) | (pg << 2) | (k & 3);
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, source lane i = 4a + b names 4
+// consecutive 16-bit elements (row a, columns 4b..4b+3 of a 4 x 16 block); result lane j
+// receives column j of that block, rows 0..3.
+__device__ __forceinline__ u32x2_t lds_tr4(const u16* p) {
+  const v4i16_t r =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)p);
+  return __builtin_bit_cast(u32x2_t, r);
 }
+
+// ---- LDS tiles ---------------------------------------------------------------------
+//
+// A tile is ROWS x D bf16 stored row-major without padding, each 16-byte chunk c of row
+// r at chunk position c ^ swz(r). With swz(r) = 2 (r % 4) + (r / 4) % 2 both read
+// patterns below touch 32 distinct banks per 128-byte LDS cycle: 16-byte row reads of 8
+// consecutive rows at one chunk, and transpose reads of 4 consecutive rows x 2 chunks.
+// swz(r + 8) == swz(r).
+__device__ __forceinline__ int swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+
+// Asynchronous global -> LDS copy of rows [row0, row0 + ROWS) of a bf16 tensor whose rows
+// are `stride` elements apart, starting at column `col0` (one head), into `tile`. Rows at
+// or past `valid` read as zero (buffer range check). Every wave of the 256-thread
+// workgroup issues its share; the data is in LDS after s_waitcnt vmcnt(0) + barrier.
+// buffer_load_dwordx4 ... lds writes lane l's 16 bytes to M0 + 16 l, so each wave
+// instruction fills 1 KB of the tile and the lane picks the global chunk that belongs at
+// its LDS position.
+template <int D, int ROWS>
+__device__ __forceinline__ void tile_copy_async(const u16* src, int64_t row0, int valid,
+                                                int64_t stride, int64_t col0, u16* tile,
+                                                int wave, int lane) {
+  constexpr int CPR = D / 8;         // chunks per row
+  constexpr int RPI = 64 / CPR;      // rows per wave instruction
+  constexpr int NI = ROWS / RPI;     // instructions per tile
+  constexpr int PER_WAVE = NI / 4;
+  static_assert(NI % 4 == 0, "tile must split over 4 waves");
+  const int vrows = valid < 0 ? 0 : (valid > ROWS ? ROWS : valid);
+  const uint32_t nbytes = vrows > 0 ? (uint32_t)(((int64_t)(vrows - 1) * stride + D) * 2) : 0u;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(src + row0 * stride + col0), (short)0, (int)nbytes, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int ins = wave * PER_WAVE + i;
+    const int r = ins * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ swz(r);
+    const int voff = (int)(((int64_t)r * stride + c * 8) * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)(tile + ins * 512), 16, voff, 0, 0, 0);
+  }
+}
+
+// Waits for this wave's outstanding vector-memory operations (the async tile copies).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// MFMA operand with lane row/column l % 32 taken from tile rows row0 .. row0 + 31 and
+// slots 16 * kc + 8 * (l / 32) + 0..7 along the row: K for S^T = K Q^T, Q or dO for
+// S = Q K^T. row0 is a multiple of 8.
+template <int D>
+__device__ __forceinline__ bf16x8_t tile_rowop(const u16* tile, int row0, int kc, int lane) {
+  const int r = row0 + (lane & 31);
+  const int c = (2 * kc + (lane >> 5)) ^ swz(r);
+  return *reinterpret_cast<const bf16x8_t*>(tile + r * D + c * 8);
+}
+
+// MFMA A operand (32 x 16) for a contraction over the ROW index of a tile: result rows
+// are tile columns c32 .. c32 + 31, contracted slots are tile rows k16 .. k16 + 15 with
+// lane half h, slot s <-> row k16 + 8 * (s / 4) + 4 * h + s % 4 -- the row order of a
+// 32x32 MFMA result, so the B operand can come straight from result registers. Built
+// from two ds_read_b64_tr_b16 (4 rows each). k16 is a multiple of 16, c32 of 32.
+template <int D>
+__device__ __forceinline__ bf16x8_t tile_trA(const u16* tile, int k16, int c32, int lane) {
+  const int j = lane & 15, grp = lane >> 4;
+  const int r = k16 + 4 * (grp >> 1) + (j >> 2);
+  const int col = c32 + 16 * (grp & 1) + 4 * (j & 3);
+  const u16* p = tile + r * D + (((col >> 3) ^ swz(r)) << 3) + (col & 7);
+  const u32x2_t lo = lds_tr4(p), hi = lds_tr4(p + 8 * D);
+  return __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+}
+
 
 }  // namespace fcp

@@ -10,15 +10,19 @@
 // Design (one workgroup = 4 waves = 256 query columns):
 //  * The scores are computed transposed, S^T = K Q^T, so each lane owns one (token,
 //    head) column: the row max / row sum of the online softmax are in-lane reductions
-//    plus one exchange between lane l and l + 32, and rescaling the accumulator is a
-//    per-lane multiply.
+//    plus one exchange between lane l and l + 32.
 //  * Q^T stays in registers for the whole item (B operand). A workgroup covers the
 //    query heads of one KV head (grouped-query attention, Sec. 2.2 and Sec. 6.1), so each
 //    K/V tile staged in LDS is reused by all of them.
-//  * O^T = V^T P^T: P comes straight from the S^T registers as the B operand; V is
-//    written to LDS transposed, with keys ordered to match the S^T result layout.
-//  * K/V tiles of 64 keys are double-buffered: global loads for tile n+1 are issued
-//    before the MFMAs of tile n and written to the other LDS buffer afterwards.
+//  * O^T = V^T P^T: P comes straight from the S^T registers as the B operand; the V^T
+//    A operand is read from the row-major V tile with the LDS transpose read.
+//  * K and V tiles move from HBM straight into (swizzled) LDS with buffer loads that
+//    bypass registers.
+//  * The running max is only raised (and the accumulator rescaled) when a new score
+//    exceeds it by more than 2^8, so in steady state the accumulator is touched by MFMAs
+//    only; P <= 2^8 meanwhile, which bf16 and fp32 hold exactly as well as P <= 1.
+//  * K/V tiles of 64 keys are double-buffered: the copy of tile n+1 is issued before
+//    the MFMAs of tile n and waited for at the end of the iteration.
 #include "fcp_common.h"
 #include "fcp_kernels.h"
 #include "fcp_types.h"
@@ -26,57 +30,8 @@
 namespace fcp {
 namespace {
 
-template <int D>
-struct KvTileLoader {
-  static constexpr int CPK = D / 8;                   // 16-byte chunks per key row
-  static constexpr int KPT = kKvTile * CPK / 256;     // keys per thread (4 or 2)
-  static constexpr int KLD = D + 8;                   // K tile row stride (elements)
-  static constexpr int VLD = kKvTile + 8;             // V^T tile row stride (elements)
-  u32x4_t rk[KPT], rv[KPT];
-  int kg, dc;
-
-  __device__ void init(int tid) {
-    kg = tid / CPK;
-    dc = tid % CPK;
-  }
-
-  __device__ void load(const u16* __restrict__ k, const u16* __restrict__ v, int64_t row_stride,
-                       int kvh, const KvSeg& s, int t) {
-#pragma unroll
-    for (int e = 0; e < KPT; ++e) {
-      const int j = t * kKvTile + kg * KPT + e;
-      if (j < s.kv_len) {
-        const int64_t off = (int64_t)(s.kv_start + j) * row_stride + (int64_t)kvh * D + dc * 8;
-        rk[e] = *reinterpret_cast<const u32x4_t*>(k + off);
-        rv[e] = *reinterpret_cast<const u32x4_t*>(v + off);
-      } else {
-        rk[e] = u32x4_t{0u, 0u, 0u, 0u};
-        rv[e] = u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
-  }
-
-  __device__ void store(u16* sK, u16* sV) const {
-#pragma unroll
-    for (int e = 0; e < KPT; ++e)
-      *reinterpret_cast<u32x4_t*>(&sK[(kg * KPT + e) * KLD + dc * 8]) = rk[e];
-    const int p = tpos(kg * KPT);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      u16* lo = &sV[(dc * 8 + 2 * w) * VLD + p];
-      u16* hi = &sV[(dc * 8 + 2 * w + 1) * VLD + p];
-      if constexpr (KPT == 4) {
-        *reinterpret_cast<u32x2_t*>(lo) =
-            u32x2_t{pack_lo(rv[0][w], rv[1][w]), pack_lo(rv[2][w], rv[3][w])};
-        *reinterpret_cast<u32x2_t*>(hi) =
-            u32x2_t{pack_hi(rv[0][w], rv[1][w]), pack_hi(rv[2][w], rv[3][w])};
-      } else {
-        *reinterpret_cast<uint32_t*>(lo) = pack_lo(rv[0][w], rv[1][w]);
-        *reinterpret_cast<uint32_t*>(hi) = pack_hi(rv[0][w], rv[1][w]);
-      }
-    }
-  }
-};
+// log2 headroom before the running max is raised.
+constexpr float kRescaleSlack = 8.0f;
 
 // Number of 64-key tiles of segment `s` visible to queries [q_off, q_off + rows).
 __device__ __forceinline__ int seg_tiles(const KvSeg& s, int q_off, int rows) {
@@ -91,10 +46,8 @@ void fwd_kernel(FwdArgs a) {
   constexpr int CB = 2;         // column blocks per wave
   constexpr int NKC = D / 16;   // k-chunks of the QK^T contraction
   constexpr int NDB = D / 32;   // d-blocks of the output
-  using Loader = KvTileLoader<D>;
-  constexpr int KLD = Loader::KLD, VLD = Loader::VLD;
-  __shared__ __attribute__((aligned(16))) u16 sK[2][kKvTile * KLD];
-  __shared__ __attribute__((aligned(16))) u16 sV[2][D * VLD];
+  __shared__ __attribute__((aligned(16))) u16 sK[2][kKvTile * D];
+  __shared__ __attribute__((aligned(16))) u16 sV[2][kKvTile * D];
 
   const int item_idx = blockIdx.x / a.n_hgroups;
   const int hg = blockIdx.x - item_idx * a.n_hgroups;
@@ -140,25 +93,23 @@ void fwd_kernel(FwdArgs a) {
   const int seg_end = it.seg_begin + it.seg_count;
   int s = it.seg_begin, t = 0, nt = 0;
   KvSeg sg{};
-  // First (segment, tile) with visible keys.
   for (; s < seg_end; ++s) {
     sg = a.segs[s];
     nt = seg_tiles(sg, it.q_off, it.q_rows);
     if (nt > 0) break;
   }
   bool have = s < seg_end;
-  Loader ld;
-  ld.init(tid);
+  const int64_t kv_col = (int64_t)kvh * D;
   if (have) {
-    ld.load(a.k, a.v, kv_stride, kvh, sg, 0);
-    ld.store(sK[0], sV[0]);
+    tile_copy_async<D, kKvTile>(a.k, sg.kv_start, sg.kv_len, kv_stride, kv_col, sK[0], wave, lane);
+    tile_copy_async<D, kKvTile>(a.v, sg.kv_start, sg.kv_len, kv_stride, kv_col, sV[0], wave, lane);
+    wait_vmem();
   }
   __syncthreads();
   int buf = 0;
   const float c = a.scale_log2;
 
   while (have) {
-    // Next tile position.
     int ns = s, ntile = t + 1, nnt = nt;
     KvSeg nsg = sg;
     if (ntile >= nnt) {
@@ -170,95 +121,102 @@ void fwd_kernel(FwdArgs a) {
       }
     }
     const bool next = ns < seg_end;
-    if (next) ld.load(a.k, a.v, kv_stride, kvh, nsg, ntile);
+    if (next) {
+      const int j0n = ntile * kKvTile;
+      tile_copy_async<D, kKvTile>(a.k, (int64_t)nsg.kv_start + j0n, nsg.kv_len - j0n, kv_stride,
+                                  kv_col, sK[buf ^ 1], wave, lane);
+      tile_copy_async<D, kKvTile>(a.v, (int64_t)nsg.kv_start + j0n, nsg.kv_len - j0n, kv_stride,
+                                  kv_col, sV[buf ^ 1], wave, lane);
+    }
 
     const u16* Kt = sK[buf];
     const u16* Vt = sV[buf];
-    // S^T = K Q^T for two 32-key blocks.
-    f32x16_t S[CB][2];
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) S[cb][0] = S[cb][1] = zero16();
-#pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      const bf16x8_t k0 =
-          *reinterpret_cast<const bf16x8_t*>(&Kt[l32 * KLD + 16 * kc + 8 * hi]);
-      const bf16x8_t k1 =
-          *reinterpret_cast<const bf16x8_t*>(&Kt[(32 + l32) * KLD + 16 * kc + 8 * hi]);
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        S[cb][0] = mfma32(k0, qb[cb][kc], S[cb][0]);
-        S[cb][1] = mfma32(k1, qb[cb][kc], S[cb][1]);
-      }
-    }
-
-    // Mask: key j (within the KV range) visible to query i iff j < kv_len and, causal,
-    // j - i <= mask_offset.
     const int j0 = t * kKvTile;
     const bool causal = sg.flags & 1;
     const bool need_mask = (j0 + kKvTile > sg.kv_len) ||
                            (causal && j0 + kKvTile - 1 - it.q_off > sg.mask_offset);
-    if (need_mask) {
+    // One 32-key block at a time: S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16_t S[CB];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) S[cb] = zero16();
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        const bf16x8_t ka = tile_rowop<D>(Kt, kb * 32, kc, lane);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) S[cb] = mfma32(ka, qb[cb][kc], S[cb]);
+      }
+      // Mask: key j (within the KV range) visible to query i iff j < kv_len and, causal,
+      // j - i <= mask_offset.
+      if (need_mask) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const int jb = j0 + kb * 32;
+          const int lim_c = sg.mask_offset + it.q_off + tok[cb] - jb;
+          const int lim = causal ? min(sg.kv_len - jb - 1, lim_c) : sg.kv_len - jb - 1;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (8 * (r >> 2) + 4 * hi + (r & 3) > lim) S[cb][r] = -INFINITY;
+        }
+      }
+      // Online softmax in base 2 with the scale folded into the exponent; the running
+      // max m is raised only when the block's max exceeds it by more than kRescaleSlack.
+      bool raise[CB];
+      float m_new[CB];
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const int i = it.q_off + tok[cb];
+        float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            const bool vis = j < sg.kv_len && (!causal || j - i <= sg.mask_offset);
-            if (!vis) S[cb][kb][r] = -INFINITY;
-          }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[cb][r]);
+        mx = fmaxf(mx, wave_xor32(mx)) * c;
+        if (m[cb] == -INFINITY) {
+          m[cb] = mx;  // nothing accumulated yet: no rescale needed
+          raise[cb] = false;
+        } else {
+          raise[cb] = mx > m[cb] + kRescaleSlack;
+        }
+        m_new[cb] = fmaxf(m[cb], mx);
       }
-    }
-
-    // Online softmax (base 2, scale folded into the exponent).
-    bf16x8_t pb[CB][2][2];
+      if (__any(raise[0] || raise[1])) {
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      float mx = -INFINITY;
+        for (int cb = 0; cb < CB; ++cb) {
+          const float alpha = raise[cb] ? __builtin_amdgcn_exp2f(m[cb] - m_new[cb]) : 1.f;
+          m[cb] = raise[cb] ? m_new[cb] : m[cb];
+          l[cb] *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+          for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[cb][kb][r]);
-      mx = fmaxf(mx, wave_xor32(mx));
-      const float m_new = fmaxf(m[cb], mx * c);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m[cb] - m_use);
-      m[cb] = m_new;
-      float rs = 0.f;
+            for (int r = 0; r < 16; ++r) acc[cb][db][r] *= alpha;
+        }
+      }
+      bf16x8_t pb[CB][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float p[16];
+      for (int cb = 0; cb < CB; ++cb) {
+        const float m_use = (m[cb] == -INFINITY) ? 0.f : m[cb];
+        // The row sum uses the fp32 values (the LSE must not carry bf16 rounding).
+        float p[16], rs = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          p[r] = __builtin_amdgcn_exp2f(fmaf(S[cb][kb][r], c, -m_use));
+          p[r] = __builtin_amdgcn_exp2f(fmaf(S[cb][r], c, -m_use));
           rs += p[r];
         }
-        pb[cb][kb][0] = to_bf16x8(p);
-        pb[cb][kb][1] = to_bf16x8(p + 8);
+        l[cb] += rs;
+        pb[cb][0] = to_bf16x8(p);
+        pb[cb][1] = to_bf16x8(p + 8);
       }
-      l[cb] = l[cb] * alpha + rs;
+      // O^T += V^T P^T over the block's 32 keys.
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[cb][db][r] *= alpha;
+        for (int half = 0; half < 2; ++half) {
+          const bf16x8_t va = tile_trA<D>(Vt, kb * 32 + 16 * half, db * 32, lane);
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) acc[cb][db] = mfma32(va, pb[cb][half], acc[cb][db]);
+        }
     }
 
-    // O^T += V^T P^T.
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(
-              &Vt[(db * 32 + l32) * VLD + kb * 32 + 16 * half + 8 * hi]);
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) acc[cb][db] = mfma32(va, pb[cb][kb][half], acc[cb][db]);
-        }
-
-    if (next) ld.store(sK[buf ^ 1], sV[buf ^ 1]);
+    wait_vmem();
     __syncthreads();
     buf ^= 1;
     s = ns;
