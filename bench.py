@@ -137,6 +137,8 @@ def kernel_work(name, wl, pairs):
         return parts * hq * (4 * d + 4) + q_rows * hq * (2 * d + 4), "byte", "hbm"
     if name == "bwd_delta":
         return q_rows * hq * (4 * d + 4), "byte", "hbm"
+    if name == "bwd_dkdv_reduce":
+        return None, "byte", "hbm"   # depends on the split; never the dominant kernel
     raise KeyError(name)
 
 

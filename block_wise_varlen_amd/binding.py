@@ -24,7 +24,7 @@ SYMBOLS = ("fcp_abi_version", "fcp_status_string", "fcp_last_error", "fcp_valida
            "fcp_workspace_bytes", "fcp_block_attn_fwd", "fcp_merge_partials",
            "fcp_block_attn_fwd_fused", "fcp_block_attn_bwd", "fcp_timing_enable",
            "fcp_timing_read", "fcp_kernel_name")
-FCP_KERNEL_COUNT = 6
+FCP_KERNEL_COUNT = 7
 
 
 class FcpError(RuntimeError):

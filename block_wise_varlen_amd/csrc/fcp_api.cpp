@@ -241,7 +241,8 @@ int fcp_timing_read(double* total_ms, int32_t* launches, int32_t n) {
 
 const char* fcp_kernel_name(int id) {
   static const char* names[FCP_KERNEL_COUNT] = {"fwd_partial", "fwd_fused", "merge",
-                                                "bwd_delta",   "bwd_dq",    "bwd_dkdv"};
+                                                "bwd_delta",   "bwd_dq",    "bwd_dkdv",
+                                                "bwd_dkdv_reduce"};
   return (id >= 0 && id < FCP_KERNEL_COUNT) ? names[id] : "";
 }
 
@@ -382,10 +383,20 @@ int fcp_block_attn_bwd(const fcp_dims_t* dims, const void* q, const void* k, con
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
+    const size_t part_floats = (size_t)P.n_slots * s.hkv * fcp::kKvTileBwd * s.d;
+    a.part_dk = reinterpret_cast<float*>(static_cast<char*>(ws) + P.off_partial);
+    a.part_dv = a.part_dk + part_floats;
+    a.reduce = at<fcp::ReduceItem>(ws, P.off_reduce);
+    a.n_reduce = P.n_reduce;
     e = timed(FCP_KERNEL_DQ, stream, [&] { return fcp::launch_bwd_dq(a, s.d, stream); });
     if (e != hipSuccess) return hip_err(e, "dQ launch");
     e = timed(FCP_KERNEL_DKDV, stream, [&] { return fcp::launch_bwd_dkdv(a, s.d, stream); });
     if (e != hipSuccess) return hip_err(e, "dK/dV launch");
+    if (P.n_reduce > 0) {
+      e = timed(FCP_KERNEL_DKDV_REDUCE, stream,
+                [&] { return fcp::launch_bwd_reduce(a, s.d, stream); });
+      if (e != hipSuccess) return hip_err(e, "dK/dV reduce launch");
+    }
     return FCP_OK;
   });
 }

@@ -12,12 +12,12 @@
 //    range), like the fused forward. Scores are computed transposed (S^T = K Q^T,
 //    dP^T = V dO^T) so each lane owns a (token, head) column; dQ^T = K^T dS^T takes dS^T
 //    straight from registers and K^T through LDS transpose reads of the K tile.
-//  * dK/dV, KV-stationary: a work item is up to 128 keys of one elementary KV interval
+//  * dK/dV, KV-stationary: a work item is up to 256 keys of one elementary KV interval
 //    (keys covered by the same set of pairs) for one KV head; it streams every 64-row Q
 //    tile of those pairs and every query head of the group. Scores are computed with
 //    keys as columns (S = Q K^T, dP = dO V^T), so P and dS feed dV^T = dO^T P and
 //    dK^T = Q^T dS from registers, with dO^T and Q^T read by LDS transpose reads of the
-//    row-major Q and dO tiles.
+//    row-major Q and dO tiles. K^T is register-resident; the item's V block stays in LDS.
 // Recomputing S and dP in both kernels costs 4 of the 14 contractions per score; the
 // counted work stays the 5 of the method.
 #include "fcp_common.h"
@@ -37,10 +37,11 @@ __device__ __forceinline__ int seg_tiles(const KvSeg& s, int q_off, int rows) {
   return last < 0 ? 0 : last / kKvTile + 1;
 }
 
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int D, int CB>
+__global__ __launch_bounds__(64 * kColBlocksPerWG / CB)
+__attribute__((amdgpu_waves_per_eu(CB == 1 ? 2 : 1, CB == 1 ? 2 : 1)))
 void dq_kernel(BwdArgs a) {
-  constexpr int CB = 2;
+  constexpr int NW = kColBlocksPerWG / CB;  // waves per workgroup
   constexpr int NKC = D / 16;
   constexpr int NDB = D / 32;
   __shared__ __attribute__((aligned(16))) u16 sK[2][kKvTile * D];
@@ -56,6 +57,7 @@ void dq_kernel(BwdArgs a) {
   const int64_t q_stride = (int64_t)a.hq * D;
   const int64_t kv_stride = (int64_t)a.hkv * D;
   const float c = a.scale_log2;
+  const TileOffsets<D> to(lane);
 
   int tok[CB], head[CB];
   bool valid[CB];
@@ -100,8 +102,10 @@ void dq_kernel(BwdArgs a) {
   bool have = s < seg_end;
   const int64_t kv_col = (int64_t)kvh * D;
   if (have) {
-    tile_copy_async<D, kKvTile>(a.k, sg.kv_start, sg.kv_len, kv_stride, kv_col, sK[0], wave, lane);
-    tile_copy_async<D, kKvTile>(a.v, sg.kv_start, sg.kv_len, kv_stride, kv_col, sV[0], wave, lane);
+    tile_copy_async<D, kKvTile, NW>(a.k, sg.kv_start, sg.kv_len, kv_stride, kv_col, sK[0], wave,
+                                    lane);
+    tile_copy_async<D, kKvTile, NW>(a.v, sg.kv_start, sg.kv_len, kv_stride, kv_col, sV[0], wave,
+                                    lane);
     wait_vmem();
   }
   __syncthreads();
@@ -121,10 +125,10 @@ void dq_kernel(BwdArgs a) {
     const bool next = ns < seg_end;
     if (next) {
       const int j0n = ntile * kKvTile;
-      tile_copy_async<D, kKvTile>(a.k, (int64_t)nsg.kv_start + j0n, nsg.kv_len - j0n, kv_stride,
-                                  kv_col, sK[buf ^ 1], wave, lane);
-      tile_copy_async<D, kKvTile>(a.v, (int64_t)nsg.kv_start + j0n, nsg.kv_len - j0n, kv_stride,
-                                  kv_col, sV[buf ^ 1], wave, lane);
+      tile_copy_async<D, kKvTile, NW>(a.k, (int64_t)nsg.kv_start + j0n, nsg.kv_len - j0n,
+                                      kv_stride, kv_col, sK[buf ^ 1], wave, lane);
+      tile_copy_async<D, kKvTile, NW>(a.v, (int64_t)nsg.kv_start + j0n, nsg.kv_len - j0n,
+                                      kv_stride, kv_col, sV[buf ^ 1], wave, lane);
     }
 
     const u16* Kt = sK[buf];
@@ -140,8 +144,8 @@ void dq_kernel(BwdArgs a) {
       for (int cb = 0; cb < CB; ++cb) S[cb] = dP[cb] = zero16();
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
-        const bf16x8_t ka = tile_rowop<D>(Kt, kb * 32, kc, lane);
-        const bf16x8_t va = tile_rowop<D>(Vt, kb * 32, kc, lane);
+        const bf16x8_t ka = to.rowop(Kt, kb * 32, kc);
+        const bf16x8_t va = to.rowop(Vt, kb * 32, kc);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
           S[cb] = mfma32(ka, qb[cb][kc], S[cb]);
@@ -169,7 +173,7 @@ void dq_kernel(BwdArgs a) {
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const bf16x8_t kt = tile_trA<D>(Kt, kb * 32 + 16 * half, db * 32, lane);
+          const bf16x8_t kt = to.trA(Kt, kb * 32 + 16 * half, db * 32);
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb) acc[cb][db] = mfma32(kt, dsb[cb][half], acc[cb][db]);
         }
@@ -207,18 +211,23 @@ void dq_kernel(BwdArgs a) {
 // dK / dV kernel
 // ---------------------------------------------------------------------------------
 
-constexpr int kQRows = 64;  // query rows per streamed tile (two 32-row MFMA blocks)
+constexpr int kQRows = kQTileBwd;  // query rows per streamed tile (two 32-row blocks)
+constexpr int kDkdvWaves = kKvTileBwd / 32;
 
 // First query of segment `s` that sees any key of the item (causal), else 0.
 __device__ __forceinline__ int first_query(const QSeg& s, int key_off) {
   return (s.flags & 1) ? max(0, key_off - s.mask_offset) : 0;
 }
 
+// 8 waves (two per SIMD), each owning 32 keys as MFMA columns. K^T stays in registers;
+// the item's V block stays in LDS for the whole item and feeds dP = dO V^T.
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dkdv_kernel(BwdArgs a) {
   constexpr int NKC = D / 16;
   constexpr int NDB = D / 32;
+  constexpr int NW = kDkdvWaves;
+  __shared__ __attribute__((aligned(16))) u16 sV[kKvTileBwd * D];
   __shared__ __attribute__((aligned(16))) u16 sQ[2][kQRows * D];
   __shared__ __attribute__((aligned(16))) u16 sG[2][kQRows * D];
   __shared__ __attribute__((aligned(16))) float sL[2][kQRows];
@@ -233,21 +242,21 @@ void dkdv_kernel(BwdArgs a) {
   const int64_t q_stride = (int64_t)a.hq * D;
   const float c = a.scale_log2;
 
-  // This lane's key column; K^T and V^T as B operands (k-slots d = 16*kc + 8*hi + 0..7).
+  const TileOffsets<D> to(lane);
+  // This lane's key column; K^T as B operand (k-slots d = 16*kc + 8*hi + 0..7).
   const int key = wave * 32 + l32;  // within the item
   const bool kvalid = key < it.kv_rows;
   const int jkey = it.key_off + key;  // within the interval
-  bf16x8_t kb[NKC], vb[NKC];
+  bf16x8_t kb[NKC];
   {
     const int64_t off = (int64_t)(it.kv_row0 + key) * kv_stride + (int64_t)kvh * D;
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
+    for (int kc = 0; kc < NKC; ++kc)
       kb[kc] = kvalid ? *reinterpret_cast<const bf16x8_t*>(a.k + off + 16 * kc + 8 * hi)
                       : zero_bf16x8();
-      vb[kc] = kvalid ? *reinterpret_cast<const bf16x8_t*>(a.v + off + 16 * kc + 8 * hi)
-                      : zero_bf16x8();
-    }
   }
+  tile_copy_async<D, kKvTileBwd, NW>(a.v, it.kv_row0, it.kv_rows, kv_stride, (int64_t)kvh * D,
+                                     sV, wave, lane);
   f32x16_t dk[NDB], dv[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = zero16();
@@ -256,7 +265,8 @@ void dkdv_kernel(BwdArgs a) {
   // query) x query heads of the group.
   const int seg_end = it.seg_begin + it.seg_count;
   const int G = a.group;
-  int s = it.seg_begin, i0 = 0, h = 0;
+  const int h_first = it.heads & 0xffff, h_end = h_first + (it.heads >> 16);
+  int s = it.seg_begin, i0 = 0, h = h_first;
   QSeg sg{};
   for (; s < seg_end; ++s) {
     sg = a.qsegs[s];
@@ -267,10 +277,10 @@ void dkdv_kernel(BwdArgs a) {
   float stat = 0.f;  // tid < 64: LSE (base 2) of row tid; 64 <= tid < 128: Delta
   auto load_tile = [&](const QSeg& q, int r0, int head, int b) {
     const int64_t col = (int64_t)head * D;
-    tile_copy_async<D, kQRows>(a.q, (int64_t)q.q_start + r0, q.q_len - r0, q_stride, col,
-                               sQ[b], wave, lane);
-    tile_copy_async<D, kQRows>(a.dout, (int64_t)q.q_start + r0, q.q_len - r0, q_stride, col,
-                               sG[b], wave, lane);
+    tile_copy_async<D, kQRows, NW>(a.q, (int64_t)q.q_start + r0, q.q_len - r0, q_stride, col,
+                                   sQ[b], wave, lane);
+    tile_copy_async<D, kQRows, NW>(a.dout, (int64_t)q.q_start + r0, q.q_len - r0, q_stride, col,
+                                   sG[b], wave, lane);
     if (tid < 2 * kQRows) {
       const int r = tid & (kQRows - 1);
       const bool ok = r0 + r < q.q_len;
@@ -290,18 +300,18 @@ void dkdv_kernel(BwdArgs a) {
       sD[b][tid - kQRows] = stat;
   };
   if (have) {
-    load_tile(sg, i0, kvh * G, 0);
+    load_tile(sg, i0, kvh * G + h_first, 0);
     store_stats(0);
-    wait_vmem();
   }
+  wait_vmem();
   __syncthreads();
   int buf = 0;
 
   while (have) {
     int ns = s, ni0 = i0, nh = h + 1;
     QSeg nsg = sg;
-    if (nh == G) {
-      nh = 0;
+    if (nh == h_end) {
+      nh = h_first;
       ni0 = i0 + kQRows;
       if (ni0 >= sg.q_len) {
         for (++ns; ns < seg_end; ++ns) {
@@ -320,14 +330,14 @@ void dkdv_kernel(BwdArgs a) {
     // Causal: query i (within the segment) sees this lane's key iff i >= jkey - offset.
     const int thr = jkey - sg.mask_offset - i0;  // tile row index threshold
     const bool need_mask = causal && (it.key_off + kKvTileBwd - 1 - sg.mask_offset > i0);
-    bf16x8_t pb[4], sb[4];
-#pragma unroll
+#pragma unroll 1
     for (int rb = 0; rb < 2; ++rb) {
+      // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys.
       f32x16_t S = zero16(), dP = zero16();
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
-        S = mfma32(tile_rowop<D>(Qt, rb * 32, kc, lane), kb[kc], S);
-        dP = mfma32(tile_rowop<D>(Gt, rb * 32, kc, lane), vb[kc], dP);
+        S = mfma32(to.rowop(Qt, rb * 32, kc), kb[kc], S);
+        dP = mfma32(to.rowop(Gt, rb * 32, kc), to.rowop(sV, wave * 32, kc), dP);
       }
       float p[16], ds[16];
 #pragma unroll
@@ -344,19 +354,17 @@ void dkdv_kernel(BwdArgs a) {
           ds[r] = pr * (dP[r] - D4[e]);
         }
       }
-      pb[2 * rb] = to_bf16x8(p);
-      pb[2 * rb + 1] = to_bf16x8(p + 8);
-      sb[2 * rb] = to_bf16x8(ds);
-      sb[2 * rb + 1] = to_bf16x8(ds + 8);
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS (contracting over the tile's 64 queries).
+      const bf16x8_t pb0 = to_bf16x8(p), pb1 = to_bf16x8(p + 8);
+      const bf16x8_t sb0 = to_bf16x8(ds), sb1 = to_bf16x8(ds + 8);
+      // dV^T += dO^T P and dK^T += Q^T dS over this block's 32 queries.
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int cq = 0; cq < 4; ++cq) {
-        dv[db] = mfma32(tile_trA<D>(Gt, 16 * cq, db * 32, lane), pb[cq], dv[db]);
-        dk[db] = mfma32(tile_trA<D>(Qt, 16 * cq, db * 32, lane), sb[cq], dk[db]);
+      for (int db = 0; db < NDB; ++db) {
+        dv[db] = mfma32(to.trA(Gt, rb * 32, db * 32), pb0, dv[db]);
+        dv[db] = mfma32(to.trA(Gt, rb * 32 + 16, db * 32), pb1, dv[db]);
+        dk[db] = mfma32(to.trA(Qt, rb * 32, db * 32), sb0, dk[db]);
+        dk[db] = mfma32(to.trA(Qt, rb * 32 + 16, db * 32), sb1, dk[db]);
       }
+    }
 
     if (next) store_stats(buf ^ 1);
     wait_vmem();
@@ -370,43 +378,98 @@ void dkdv_kernel(BwdArgs a) {
   }
 
   if (!kvalid) return;
-  const int64_t base = ((int64_t)(it.kv_row0 + key) * a.hkv + kvh) * D;
+  if (it.slot < 0) {
+    const int64_t base = ((int64_t)(it.kv_row0 + key) * a.hkv + kvh) * D;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d = db * 32 + 8 * g4 + 4 * hi;
-      f32x4_t ck = *reinterpret_cast<f32x4_t*>(a.dk + base + d);
-      f32x4_t cv = *reinterpret_cast<f32x4_t*>(a.dv + base + d);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + 8 * g4 + 4 * hi;
+        f32x4_t ck = *reinterpret_cast<f32x4_t*>(a.dk + base + d);
+        f32x4_t cv = *reinterpret_cast<f32x4_t*>(a.dv + base + d);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ck[e] += a.scale * dk[db][4 * g4 + e];
-        cv[e] += dv[db][4 * g4 + e];
+        for (int e = 0; e < 4; ++e) {
+          ck[e] += a.scale * dk[db][4 * g4 + e];
+          cv[e] += dv[db][4 * g4 + e];
+        }
+        *reinterpret_cast<f32x4_t*>(a.dk + base + d) = ck;
+        *reinterpret_cast<f32x4_t*>(a.dv + base + d) = cv;
       }
-      *reinterpret_cast<f32x4_t*>(a.dk + base + d) = ck;
-      *reinterpret_cast<f32x4_t*>(a.dv + base + d) = cv;
+  } else {
+    // Part of a split item: write this part's (scaled) sums to its slot.
+    const int64_t base = (((int64_t)it.slot * a.hkv + kvh) * kKvTileBwd + key) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + 8 * g4 + 4 * hi;
+        f32x4_t ck, cv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ck[e] = a.scale * dk[db][4 * g4 + e];
+          cv[e] = dv[db][4 * g4 + e];
+        }
+        *reinterpret_cast<f32x4_t*>(a.part_dk + base + d) = ck;
+        *reinterpret_cast<f32x4_t*>(a.part_dv + base + d) = cv;
+      }
+  }
+}
+
+// Adds the partial slots of each split dK/dV item into dk/dv, slots in increasing order
+// (deterministic). One workgroup per (item, KV head); HBM-bound.
+template <int D>
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(BwdArgs a) {
+  const int ridx = blockIdx.x / a.hkv;
+  const int kvh = blockIdx.x - ridx * a.hkv;
+  const ReduceItem r = a.reduce[ridx];
+  constexpr int V4 = D / 4;
+  const int total = r.kv_rows * V4;
+  for (int e = threadIdx.x; e < total; e += 256) {
+    const int key = e / V4, d4 = e - key * V4;
+    f32x4_t sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < r.n_slots; ++p) {
+      const int64_t src = (((int64_t)(r.slot_begin + p) * a.hkv + kvh) * kKvTileBwd + key) * V4 + d4;
+      sk += reinterpret_cast<const f32x4_t*>(a.part_dk)[src];
+      sv += reinterpret_cast<const f32x4_t*>(a.part_dv)[src];
     }
+    const int64_t dst = ((int64_t)(r.kv_row0 + key) * a.hkv + kvh) * V4 + d4;
+    reinterpret_cast<f32x4_t*>(a.dk)[dst] += sk;
+    reinterpret_cast<f32x4_t*>(a.dv)[dst] += sv;
+  }
 }
 
 }  // namespace
 
+// Column blocks per wave of the launched dQ kernel (see the forward's kFwdCB).
+constexpr int kDqCB = 1;
+
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t stream) {
   if (a.n_qitems == 0) return hipSuccess;
-  const dim3 grid((unsigned)a.n_qitems * (unsigned)a.n_hgroups), block(256);
+  const dim3 grid((unsigned)a.n_qitems * (unsigned)a.n_hgroups), block(64 * kColBlocksPerWG / kDqCB);
   if (head_dim == 128)
-    hipLaunchKernelGGL((dq_kernel<128>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((dq_kernel<128, kDqCB>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((dq_kernel<64>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((dq_kernel<64, kDqCB>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t stream) {
   if (a.n_kvitems == 0) return hipSuccess;
-  const dim3 grid((unsigned)a.n_kvitems * (unsigned)a.hkv), block(256);
+  const dim3 grid((unsigned)a.n_kvitems * (unsigned)a.hkv), block(64 * kDkdvWaves);
   if (head_dim == 128)
     hipLaunchKernelGGL((dkdv_kernel<128>), grid, block, 0, stream, a);
   else
     hipLaunchKernelGGL((dkdv_kernel<64>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_reduce(const BwdArgs& a, int head_dim, hipStream_t stream) {
+  if (a.n_reduce == 0) return hipSuccess;
+  const dim3 grid((unsigned)a.n_reduce * (unsigned)a.hkv), block(256);
+  if (head_dim == 128)
+    hipLaunchKernelGGL((dkdv_reduce_kernel<128>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((dkdv_reduce_kernel<64>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -84,20 +84,20 @@ __device__ __forceinline__ int swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1);
 
 // Asynchronous global -> LDS copy of rows [row0, row0 + ROWS) of a bf16 tensor whose rows
 // are `stride` elements apart, starting at column `col0` (one head), into `tile`. Rows at
-// or past `valid` read as zero (buffer range check). Every wave of the 256-thread
+// or past `valid` read as zero (buffer range check). Every wave of the NW-wave
 // workgroup issues its share; the data is in LDS after s_waitcnt vmcnt(0) + barrier.
 // buffer_load_dwordx4 ... lds writes lane l's 16 bytes to M0 + 16 l, so each wave
 // instruction fills 1 KB of the tile and the lane picks the global chunk that belongs at
 // its LDS position.
-template <int D, int ROWS>
+template <int D, int ROWS, int NW = 4>
 __device__ __forceinline__ void tile_copy_async(const u16* src, int64_t row0, int valid,
                                                 int64_t stride, int64_t col0, u16* tile,
                                                 int wave, int lane) {
   constexpr int CPR = D / 8;         // chunks per row
   constexpr int RPI = 64 / CPR;      // rows per wave instruction
   constexpr int NI = ROWS / RPI;     // instructions per tile
-  constexpr int PER_WAVE = NI / 4;
-  static_assert(NI % 4 == 0, "tile must split over 4 waves");
+  constexpr int PER_WAVE = NI / NW;
+  static_assert(NI % NW == 0, "tile must split over the waves");
   const int vrows = valid < 0 ? 0 : (valid > ROWS ? ROWS : valid);
   const uint32_t nbytes = vrows > 0 ? (uint32_t)(((int64_t)(vrows - 1) * stride + D) * 2) : 0u;
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -113,33 +113,43 @@ __device__ __forceinline__ void tile_copy_async(const u16* src, int64_t row0, in
   }
 }
 
+// MFMA operand reads from a swizzled tile, with the per-lane LDS element offsets shared
+// by every tile a lane reads (6 registers in all).
+//  * rowop(tile, row0, kc): lane row/column l % 32 taken from tile row row0 + l % 32,
+//    slots 16 kc + 8 (l / 32) + 0..7 along the row (row0 % 8 == 0): K for S^T = K Q^T,
+//    Q or dO for S = Q K^T. It sits at row0 * D + row[kc % 4] + 64 (kc / 4).
+//  * trA(tile, k16, c32): the A operand (32 x 16) of a contraction over the tile's ROW
+//    index: result rows are tile columns c32 .. c32 + 31, slot s of lane half h is tile
+//    row k16 + 8 (s / 4) + 4 h + s % 4 -- the row order of a 32x32 MFMA result, so the
+//    B operand can come straight from result registers. Two ds_read_b64_tr_b16 of 4 rows
+//    each, at k16 * D + tr[(c32 / 32) % 2] + 64 (c32 / 64) and 8 D further
+//    (k16 % 16 == 0, c32 % 32 == 0).
+template <int D>
+struct TileOffsets {
+  int row[4];
+  int tr[2];
+  __device__ explicit TileOffsets(int lane) {
+    const int r = lane & 31, s = swz(r), h = lane >> 5;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) row[kc] = r * D + (((2 * kc + h) ^ s) << 3);
+    const int j = lane & 15, grp = lane >> 4;
+    const int tr_r = 4 * (grp >> 1) + (j >> 2);
+    const int x = 2 * (grp & 1) + ((j & 3) >> 1);  // chunk within a 32-column block
+#pragma unroll
+    for (int odd = 0; odd < 2; ++odd)
+      tr[odd] = tr_r * D + (((4 * odd + x) ^ swz(tr_r)) << 3) + 4 * (j & 1);
+  }
+  __device__ __forceinline__ bf16x8_t rowop(const u16* tile, int row0, int kc) const {
+    return *reinterpret_cast<const bf16x8_t*>(tile + row0 * D + row[kc & 3] + 64 * (kc >> 2));
+  }
+  __device__ __forceinline__ bf16x8_t trA(const u16* tile, int k16, int c32) const {
+    const u16* p = tile + k16 * D + tr[(c32 >> 5) & 1] + 64 * (c32 >> 6);
+    const u32x2_t lo = lds_tr4(p), hi = lds_tr4(p + 8 * D);
+    return __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+  }
+};
+
 // Waits for this wave's outstanding vector-memory operations (the async tile copies).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
-
-// MFMA operand with lane row/column l % 32 taken from tile rows row0 .. row0 + 31 and
-// slots 16 * kc + 8 * (l / 32) + 0..7 along the row: K for S^T = K Q^T, Q or dO for
-// S = Q K^T. row0 is a multiple of 8.
-template <int D>
-__device__ __forceinline__ bf16x8_t tile_rowop(const u16* tile, int row0, int kc, int lane) {
-  const int r = row0 + (lane & 31);
-  const int c = (2 * kc + (lane >> 5)) ^ swz(r);
-  return *reinterpret_cast<const bf16x8_t*>(tile + r * D + c * 8);
-}
-
-// MFMA A operand (32 x 16) for a contraction over the ROW index of a tile: result rows
-// are tile columns c32 .. c32 + 31, contracted slots are tile rows k16 .. k16 + 15 with
-// lane half h, slot s <-> row k16 + 8 * (s / 4) + 4 * h + s % 4 -- the row order of a
-// 32x32 MFMA result, so the B operand can come straight from result registers. Built
-// from two ds_read_b64_tr_b16 (4 rows each). k16 is a multiple of 16, c32 of 32.
-template <int D>
-__device__ __forceinline__ bf16x8_t tile_trA(const u16* tile, int k16, int c32, int lane) {
-  const int j = lane & 15, grp = lane >> 4;
-  const int r = k16 + 4 * (grp >> 1) + (j >> 2);
-  const int col = c32 + 16 * (grp & 1) + 4 * (j & 3);
-  const u16* p = tile + r * D + (((col >> 3) ^ swz(r)) << 3) + (col & 7);
-  const u32x2_t lo = lds_tr4(p), hi = lds_tr4(p + 8 * D);
-  return __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
-}
-
 
 }  // namespace fcp

@@ -7,7 +7,7 @@
 // per item it writes that pair's normalised partial and its LSE (the per-slice result
 // of Sec. 2.2); with all KV ranges of a Q range it writes the final output directly.
 //
-// Design (one workgroup = 4 waves = 256 query columns):
+// Design (one workgroup = 256 query columns, 8 waves of one 32-column block each):
 //  * The scores are computed transposed, S^T = K Q^T, so each lane owns one (token,
 //    head) column: the row max / row sum of the online softmax are in-lane reductions
 //    plus one exchange between lane l and l + 32.
@@ -40,10 +40,11 @@ __device__ __forceinline__ int seg_tiles(const KvSeg& s, int q_off, int rows) {
   return last < 0 ? 0 : last / kKvTile + 1;
 }
 
-template <int D, bool FINAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int D, bool FINAL, int CB>
+__global__ __launch_bounds__(64 * kColBlocksPerWG / CB)
+__attribute__((amdgpu_waves_per_eu(CB == 1 ? 2 : 1, CB == 1 ? 2 : 1)))
 void fwd_kernel(FwdArgs a) {
-  constexpr int CB = 2;         // column blocks per wave
+  constexpr int NW = kColBlocksPerWG / CB;  // waves per workgroup
   constexpr int NKC = D / 16;   // k-chunks of the QK^T contraction
   constexpr int NDB = D / 32;   // d-blocks of the output
   __shared__ __attribute__((aligned(16))) u16 sK[2][kKvTile * D];
@@ -58,6 +59,7 @@ void fwd_kernel(FwdArgs a) {
   const int l32 = lane & 31, hi = lane >> 5;
   const int64_t q_stride = (int64_t)a.hq * D;
   const int64_t kv_stride = (int64_t)a.hkv * D;
+  const TileOffsets<D> to(lane);
 
   int tok[CB], head[CB];
   bool valid[CB];
@@ -101,8 +103,10 @@ void fwd_kernel(FwdArgs a) {
   bool have = s < seg_end;
   const int64_t kv_col = (int64_t)kvh * D;
   if (have) {
-    tile_copy_async<D, kKvTile>(a.k, sg.kv_start, sg.kv_len, kv_stride, kv_col, sK[0], wave, lane);
-    tile_copy_async<D, kKvTile>(a.v, sg.kv_start, sg.kv_len, kv_stride, kv_col, sV[0], wave, lane);
+    tile_copy_async<D, kKvTile, NW>(a.k, sg.kv_start, sg.kv_len, kv_stride, kv_col, sK[0], wave,
+                                    lane);
+    tile_copy_async<D, kKvTile, NW>(a.v, sg.kv_start, sg.kv_len, kv_stride, kv_col, sV[0], wave,
+                                    lane);
     wait_vmem();
   }
   __syncthreads();
@@ -123,10 +127,10 @@ void fwd_kernel(FwdArgs a) {
     const bool next = ns < seg_end;
     if (next) {
       const int j0n = ntile * kKvTile;
-      tile_copy_async<D, kKvTile>(a.k, (int64_t)nsg.kv_start + j0n, nsg.kv_len - j0n, kv_stride,
-                                  kv_col, sK[buf ^ 1], wave, lane);
-      tile_copy_async<D, kKvTile>(a.v, (int64_t)nsg.kv_start + j0n, nsg.kv_len - j0n, kv_stride,
-                                  kv_col, sV[buf ^ 1], wave, lane);
+      tile_copy_async<D, kKvTile, NW>(a.k, (int64_t)nsg.kv_start + j0n, nsg.kv_len - j0n,
+                                      kv_stride, kv_col, sK[buf ^ 1], wave, lane);
+      tile_copy_async<D, kKvTile, NW>(a.v, (int64_t)nsg.kv_start + j0n, nsg.kv_len - j0n,
+                                      kv_stride, kv_col, sV[buf ^ 1], wave, lane);
     }
 
     const u16* Kt = sK[buf];
@@ -143,7 +147,7 @@ void fwd_kernel(FwdArgs a) {
       for (int cb = 0; cb < CB; ++cb) S[cb] = zero16();
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
-        const bf16x8_t ka = tile_rowop<D>(Kt, kb * 32, kc, lane);
+        const bf16x8_t ka = to.rowop(Kt, kb * 32, kc);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) S[cb] = mfma32(ka, qb[cb][kc], S[cb]);
       }
@@ -178,7 +182,10 @@ void fwd_kernel(FwdArgs a) {
         }
         m_new[cb] = fmaxf(m[cb], mx);
       }
-      if (__any(raise[0] || raise[1])) {
+      bool any_raise = false;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) any_raise = any_raise || raise[cb];
+      if (__any(any_raise)) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
           const float alpha = raise[cb] ? __builtin_amdgcn_exp2f(m[cb] - m_new[cb]) : 1.f;
@@ -210,7 +217,7 @@ void fwd_kernel(FwdArgs a) {
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const bf16x8_t va = tile_trA<D>(Vt, kb * 32 + 16 * half, db * 32, lane);
+          const bf16x8_t va = to.trA(Vt, kb * 32 + 16 * half, db * 32);
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb) acc[cb][db] = mfma32(va, pb[cb][half], acc[cb][db]);
         }
@@ -261,19 +268,23 @@ void fwd_kernel(FwdArgs a) {
 
 }  // namespace
 
+// Column blocks per wave of the launched forward: 1 (8 waves, two per SIMD, so one
+// wave's softmax overlaps the other's MFMAs) or 2 (4 waves, one per SIMD).
+constexpr int kFwdCB = 1;
+
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool final_out, hipStream_t stream) {
   if (a.n_items == 0) return hipSuccess;
-  const dim3 grid((unsigned)a.n_items * (unsigned)a.n_hgroups), block(256);
+  const dim3 grid((unsigned)a.n_items * (unsigned)a.n_hgroups), block(64 * kColBlocksPerWG / kFwdCB);
   if (head_dim == 128) {
     if (final_out)
-      hipLaunchKernelGGL((fwd_kernel<128, true>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((fwd_kernel<128, true, kFwdCB>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((fwd_kernel<128, false>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((fwd_kernel<128, false, kFwdCB>), grid, block, 0, stream, a);
   } else {
     if (final_out)
-      hipLaunchKernelGGL((fwd_kernel<64, true>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((fwd_kernel<64, true, kFwdCB>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((fwd_kernel<64, false>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((fwd_kernel<64, false, kFwdCB>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }

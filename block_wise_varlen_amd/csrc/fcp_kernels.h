@@ -61,6 +61,10 @@ struct BwdArgs {
   float* dq;         // fp32 [q_rows, hq, D]   (+=)
   float* dk;         // fp32 [kv_rows, hkv, D] (+=)
   float* dv;         // fp32 [kv_rows, hkv, D] (+=)
+  float* part_dk;    // fp32 [slots, hkv, kKvTileBwd, D] partials of split items
+  float* part_dv;
+  const ReduceItem* reduce;
+  int n_reduce;
 };
 
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool final_out, hipStream_t stream);
@@ -68,5 +72,6 @@ hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_delta(const DeltaArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_bwd_reduce(const BwdArgs& a, int head_dim, hipStream_t stream);
 
 }  // namespace fcp

@@ -18,6 +18,8 @@ namespace fcp {
 namespace {
 
 constexpr size_t kAlign = 256;
+// Compute units of the target GPU, for load-balancing decisions only.
+constexpr int64_t kTargetCUs = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -308,6 +310,40 @@ int make_plan(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t n_pairs, 
         kvitems.push_back(it);
       }
     }
+    // Each item streams (Q tile, query head) steps. An item far above the average load
+    // per CU would set the makespan on its own, so heavy items are split by query-head
+    // subsets (contributions of different heads add); their parts write fp32 partials
+    // that a reduction adds into dk/dv in a fixed order.
+    int64_t total = 0;
+    for (KvItem& it : kvitems) {
+      it.cost *= s.group;
+      total += (int64_t)it.cost * s.hkv;
+    }
+    const int64_t target = std::max<int64_t>(1, total / (2 * kTargetCUs));
+    std::vector<KvItem> split;
+    std::vector<ReduceItem> reduce;
+    int32_t n_slots = 0;
+    for (const KvItem& it : kvitems) {
+      const int parts = (int)std::min<int64_t>(s.group, (it.cost + target - 1) / target);
+      if (parts <= 1) {
+        KvItem one = it;
+        one.heads = 0 | (s.group << 16);
+        one.slot = -1;
+        split.push_back(one);
+        continue;
+      }
+      reduce.push_back(ReduceItem{it.kv_row0, it.kv_rows, n_slots, parts});
+      for (int k = 0; k < parts; ++k) {
+        const int h0 = k * s.group / parts, h1 = (k + 1) * s.group / parts;
+        KvItem part = it;
+        part.heads = h0 | ((h1 - h0) << 16);
+        part.cost = it.cost / s.group * (h1 - h0);
+        part.slot = n_slots + k;
+        split.push_back(part);
+      }
+      n_slots += parts;
+    }
+    kvitems.swap(split);
     std::stable_sort(kvitems.begin(), kvitems.end(),
                      [](const KvItem& x, const KvItem& y) { return x.cost > y.cost; });
     P.off_qitems = put(&P.blob, items);
@@ -315,11 +351,17 @@ int make_plan(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t n_pairs, 
     P.off_rows = put(&P.blob, rows);
     P.off_kvitems = put(&P.blob, kvitems);
     P.off_qsegs = put(&P.blob, qsegs);
+    P.off_reduce = put(&P.blob, reduce);
     P.n_qitems = (int)items.size();
     P.n_rows = (int)rows.size();
     P.n_kvitems = (int)kvitems.size();
+    P.n_reduce = (int)reduce.size();
+    P.n_slots = n_slots;
     P.off_delta = align_up(P.blob.size());
-    P.ws_bytes = P.off_delta + align_up((size_t)dims->q_rows * s.hq * sizeof(float));
+    P.off_partial = P.off_delta + align_up((size_t)dims->q_rows * s.hq * sizeof(float));
+    // Partial slots: dK then dV, each [slot][kv head][kKvTileBwd][D] fp32.
+    P.ws_bytes = P.off_partial +
+                 align_up(2 * (size_t)n_slots * s.hkv * kKvTileBwd * s.d * sizeof(float));
     return FCP_OK;
   }
   P.ws_bytes = align_up(P.blob.size());

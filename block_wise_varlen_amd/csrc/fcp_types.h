@@ -15,10 +15,10 @@ constexpr int kColBlock = 32;
 constexpr int kColBlocksPerWG = 8;
 // Keys per KV tile of the forward and dQ kernels.
 constexpr int kKvTile = 64;
-// Keys per workgroup tile of the dK/dV kernel (4 waves x 32 keys).
-constexpr int kKvTileBwd = 128;
+// Keys per workgroup tile of the dK/dV kernel (8 waves x 32 keys).
+constexpr int kKvTileBwd = 256;
 // Query rows per Q tile streamed by the dK/dV kernel.
-constexpr int kQTileBwd = 32;
+constexpr int kQTileBwd = 64;
 
 // One forward / dQ work item: a tile of up to `q_rows` consecutive query rows of one
 // Q range, for one group of query heads (the head group comes from the grid), against
@@ -55,14 +55,23 @@ struct RowItem {
 // (a run of keys covered by the same set of pairs), for one KV head (from the grid),
 // against the Q sides qseg[seg_begin .. seg_begin + seg_count).
 struct KvItem {
-  int32_t kv_row0;    // first key row (absolute)
-  int32_t kv_rows;    // valid keys (<= kKvTileBwd)
-  int32_t key_off;    // offset of kv_row0 within its interval (key index j base)
+  int32_t kv_row0;     // first key row (absolute)
+  int32_t kv_rows;     // valid keys (<= kKvTileBwd)
+  int32_t key_off;     // offset of kv_row0 within its interval (key index j base)
   int32_t seg_begin;
   int32_t seg_count;
-  int32_t cost;
-  int32_t pad0;
-  int32_t pad1;
+  int32_t cost;        // streamed (Q tile, head) steps
+  int32_t heads;       // query heads of the group this item streams: first | count << 16
+  int32_t slot;        // -1: add into dk/dv; else partial slot (reduced afterwards)
+};
+
+// Sum of the partial slots slot_begin .. slot_begin + n_slots - 1 of one KV tile, added
+// into dk/dv rows kv_row0 .. kv_row0 + kv_rows - 1 (one KV head per workgroup).
+struct ReduceItem {
+  int32_t kv_row0;
+  int32_t kv_rows;
+  int32_t slot_begin;
+  int32_t n_slots;
 };
 
 // Q side of one pair as seen from an elementary KV interval. Key index j counts from

@@ -195,7 +195,8 @@ int fcp_block_attn_bwd(const fcp_dims_t* dims, const void* q, const void* k, con
 /*
  * Optional per-kernel timing, for measurement tools (not needed for computing).
  * Kernel ids: FCP_KERNEL_FWD (per-pair forward), FCP_KERNEL_FWD_FUSED, FCP_KERNEL_MERGE,
- * FCP_KERNEL_DELTA (backward preprocessing), FCP_KERNEL_DQ, FCP_KERNEL_DKDV.
+ * FCP_KERNEL_DELTA (backward preprocessing), FCP_KERNEL_DQ, FCP_KERNEL_DKDV,
+ * FCP_KERNEL_DKDV_REDUCE (sums the parts of dK/dV tiles the scheduler split by head).
  * fcp_timing_enable(1): from now on every kernel launch, from any thread, is bracketed by
  * a pair of HIP events recorded on the call's stream. fcp_timing_enable(0) stops that.
  * fcp_timing_read(): waits for every recorded pair, adds each pair's elapsed time to
@@ -209,7 +210,8 @@ int fcp_block_attn_bwd(const fcp_dims_t* dims, const void* q, const void* k, con
 #define FCP_KERNEL_DELTA 3
 #define FCP_KERNEL_DQ 4
 #define FCP_KERNEL_DKDV 5
-#define FCP_KERNEL_COUNT 6
+#define FCP_KERNEL_DKDV_REDUCE 6
+#define FCP_KERNEL_COUNT 7
 
 int fcp_timing_enable(int on);
 int fcp_timing_read(double* total_ms, int32_t* launches, int32_t n);
