@@ -126,10 +126,10 @@ hipError_t timed(int id, hipStream_t stream, F&& launch) {
       e = take_event();
     }
   }
-  if (b && e) hipEventRecord(b, stream);
+  if (b && e) (void)hipEventRecord(b, stream);
   const hipError_t err = launch();
   if (b && e) {
-    hipEventRecord(e, stream);
+    (void)hipEventRecord(e, stream);
     std::lock_guard<std::mutex> lk(g_time_mu);
     g_time_pending.push_back(TimedLaunch{id, b, e});
   }

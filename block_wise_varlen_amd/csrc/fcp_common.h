@@ -59,7 +59,20 @@ __device__ __forceinline__ u16 f32_to_bf16(float x) {
   return __builtin_bit_cast(u16, b);
 }
 
-__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Max / sum of x over lanes l % 32 and l % 32 + 32 (the two halves of a 32x32 MFMA result
+// column), in every lane. v_permlane32_swap exchanges the upper half of one operand with
+// the lower half of the other, so its two results hold x[l % 32] and x[l % 32 + 32];
+// no LDS round trip.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -151,5 +164,19 @@ struct TileOffsets {
 
 // Waits for this wave's outstanding vector-memory operations (the async tile copies).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Waits until at most N of this wave's vector-memory loads are outstanding (loads
+// complete in issue order), leaving the export and LDS/scalar counters unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Number of buffer_load ... lds instructions one wave issues for one tile_copy_async.
+template <int D, int ROWS, int NW>
+constexpr int tile_copy_insts() {
+  return ROWS / (64 / (D / 8)) / NW;
+}
 
 }  // namespace fcp

@@ -21,8 +21,8 @@
 //  * The running max is only raised (and the accumulator rescaled) when a new score
 //    exceeds it by more than 2^8, so in steady state the accumulator is touched by MFMAs
 //    only; P <= 2^8 meanwhile, which bf16 and fp32 hold exactly as well as P <= 1.
-//  * K/V tiles of 64 keys are double-buffered: the copy of tile n+1 is issued before
-//    the MFMAs of tile n and waited for at the end of the iteration.
+//  * K/V tiles of 64 keys go through a 3-deep LDS ring: the copy of tile n+2 is issued
+//    before the MFMAs of tile n, and tile n+1 is waited for at the end of the iteration.
 #include "fcp_common.h"
 #include "fcp_kernels.h"
 #include "fcp_types.h"
@@ -33,12 +33,51 @@ namespace {
 // log2 headroom before the running max is raised.
 constexpr float kRescaleSlack = 8.0f;
 
-// Number of 64-key tiles of segment `s` visible to queries [q_off, q_off + rows).
+// Keys per K/V tile of the forward and depth of its LDS ring.
+#ifndef FCP_FWD_KT
+#define FCP_FWD_KT 128
+#endif
+constexpr int kFwdKt = FCP_FWD_KT;
+constexpr int kFwdBuf = kFwdKt == 64 ? 3 : 2;
+
+// Number of kFwdKt-key tiles of segment `s` visible to queries [q_off, q_off + rows).
 __device__ __forceinline__ int seg_tiles(const KvSeg& s, int q_off, int rows) {
   int last = s.kv_len - 1;
   if (s.flags & 1) last = min(last, q_off + rows - 1 + s.mask_offset);
-  return last < 0 ? 0 : last / kKvTile + 1;
+  return last < 0 ? 0 : last / kFwdKt + 1;
 }
+
+// Position in the flattened (KV segment, 64-key tile) sequence of one work item, over
+// the tiles visible to queries [q_off, q_off + rows).
+struct TileCursor {
+  KvSeg sg;
+  int s, t, nt;
+  bool valid;
+  __device__ static TileCursor first(const KvSeg* segs, int s0, int s_end, int q_off,
+                                     int rows) {
+    TileCursor c{};
+    c.valid = false;
+    for (c.s = s0; c.s < s_end; ++c.s) {
+      c.sg = segs[c.s];
+      c.nt = seg_tiles(c.sg, q_off, rows);
+      if (c.nt > 0) {
+        c.valid = true;
+        c.t = 0;
+        break;
+      }
+    }
+    return c;
+  }
+  __device__ TileCursor next(const KvSeg* segs, int s_end, int q_off, int rows) const {
+    if (!valid) return *this;
+    if (t + 1 < nt) {
+      TileCursor c = *this;
+      c.t = t + 1;
+      return c;
+    }
+    return first(segs, s + 1, s_end, q_off, rows);
+  }
+};
 
 template <int D, bool FINAL, int CB>
 __global__ __launch_bounds__(64 * kColBlocksPerWG / CB)
@@ -47,8 +86,10 @@ void fwd_kernel(FwdArgs a) {
   constexpr int NW = kColBlocksPerWG / CB;  // waves per workgroup
   constexpr int NKC = D / 16;   // k-chunks of the QK^T contraction
   constexpr int NDB = D / 32;   // d-blocks of the output
-  __shared__ __attribute__((aligned(16))) u16 sK[2][kKvTile * D];
-  __shared__ __attribute__((aligned(16))) u16 sV[2][kKvTile * D];
+  constexpr int NBUF = kFwdBuf;  // tile ring depth
+  constexpr int COPY_INSTS = 2 * tile_copy_insts<D, kFwdKt, NW>();
+  __shared__ __attribute__((aligned(16))) u16 sK[NBUF][kFwdKt * D];
+  __shared__ __attribute__((aligned(16))) u16 sV[NBUF][kFwdKt * D];
 
   const int item_idx = blockIdx.x / a.n_hgroups;
   const int hg = blockIdx.x - item_idx * a.n_hgroups;
@@ -93,63 +134,69 @@ void fwd_kernel(FwdArgs a) {
   }
 
   const int seg_end = it.seg_begin + it.seg_count;
-  int s = it.seg_begin, t = 0, nt = 0;
-  KvSeg sg{};
-  for (; s < seg_end; ++s) {
-    sg = a.segs[s];
-    nt = seg_tiles(sg, it.q_off, it.q_rows);
-    if (nt > 0) break;
-  }
-  bool have = s < seg_end;
   const int64_t kv_col = (int64_t)kvh * D;
-  if (have) {
-    tile_copy_async<D, kKvTile, NW>(a.k, sg.kv_start, sg.kv_len, kv_stride, kv_col, sK[0], wave,
-                                    lane);
-    tile_copy_async<D, kKvTile, NW>(a.v, sg.kv_start, sg.kv_len, kv_stride, kv_col, sV[0], wave,
-                                    lane);
+  // Cursors over the flattened (segment, tile) sequence: the tile being computed and the
+  // two after it, whose copies are in flight.
+  TileCursor cur = TileCursor::first(a.segs, it.seg_begin, seg_end, it.q_off, it.q_rows);
+  TileCursor nx1 = cur.next(a.segs, seg_end, it.q_off, it.q_rows);
+  TileCursor nx2 = nx1.next(a.segs, seg_end, it.q_off, it.q_rows);
+  auto copy = [&](const TileCursor& tc, int b) {
+    const int j0n = tc.t * kFwdKt;
+    tile_copy_async<D, kFwdKt, NW>(a.k, (int64_t)tc.sg.kv_start + j0n, tc.sg.kv_len - j0n,
+                                   kv_stride, kv_col, sK[b], wave, lane);
+    tile_copy_async<D, kFwdKt, NW>(a.v, (int64_t)tc.sg.kv_start + j0n, tc.sg.kv_len - j0n,
+                                   kv_stride, kv_col, sV[b], wave, lane);
+  };
+  if (cur.valid) copy(cur, 0);
+  if (NBUF == 3 && nx1.valid) copy(nx1, 1);
+  if (NBUF == 3 && nx1.valid)
+    wait_vmem_le<COPY_INSTS>();
+  else
     wait_vmem();
-  }
   __syncthreads();
   int buf = 0;
   const float c = a.scale_log2;
 
-  while (have) {
-    int ns = s, ntile = t + 1, nnt = nt;
-    KvSeg nsg = sg;
-    if (ntile >= nnt) {
-      ntile = 0;
-      for (++ns; ns < seg_end; ++ns) {
-        nsg = a.segs[ns];
-        nnt = seg_tiles(nsg, it.q_off, it.q_rows);
-        if (nnt > 0) break;
-      }
+  while (cur.valid) {
+    // The ring slot after the in-flight ones was last read in the previous iteration,
+    // which every wave has left (barrier), so the next copy may overwrite it.
+    if (NBUF == 3) {
+      if (nx2.valid) copy(nx2, buf == 0 ? 2 : buf - 1);
+    } else {
+      if (nx1.valid) copy(nx1, buf ^ 1);
     }
-    const bool next = ns < seg_end;
-    if (next) {
-      const int j0n = ntile * kKvTile;
-      tile_copy_async<D, kKvTile, NW>(a.k, (int64_t)nsg.kv_start + j0n, nsg.kv_len - j0n,
-                                      kv_stride, kv_col, sK[buf ^ 1], wave, lane);
-      tile_copy_async<D, kKvTile, NW>(a.v, (int64_t)nsg.kv_start + j0n, nsg.kv_len - j0n,
-                                      kv_stride, kv_col, sV[buf ^ 1], wave, lane);
-    }
+    const KvSeg sg = cur.sg;
+    const int t = cur.t;
 
     const u16* Kt = sK[buf];
     const u16* Vt = sV[buf];
-    const int j0 = t * kKvTile;
+    const int j0 = t * kFwdKt;
     const bool causal = sg.flags & 1;
-    const bool need_mask = (j0 + kKvTile > sg.kv_len) ||
-                           (causal && j0 + kKvTile - 1 - it.q_off > sg.mask_offset);
-    // One 32-key block at a time: S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
+    const bool need_mask = (j0 + kFwdKt > sg.kv_len) ||
+                           (causal && j0 + kFwdKt - 1 - it.q_off > sg.mask_offset);
+    // 32-key blocks, software-pipelined: the S^T = K Q^T MFMAs of block kb + 1 are issued
+    // before the softmax of block kb, so the matrix pipe works while the VALU does.
+    constexpr int NKB = kFwdKt / 32;
+    f32x16_t Sn[CB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int cb = 0; cb < CB; ++cb) {
+      Sn[cb] = zero16();
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) Sn[cb] = mfma32(to.rowop(Kt, 0, kc), qb[cb][kc], Sn[cb]);
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
       f32x16_t S[CB];
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) S[cb] = zero16();
+      for (int cb = 0; cb < CB; ++cb) S[cb] = Sn[cb];
+      if (kb + 1 < NKB) {
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        const bf16x8_t ka = to.rowop(Kt, kb * 32, kc);
+        for (int cb = 0; cb < CB; ++cb) {
+          Sn[cb] = zero16();
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) S[cb] = mfma32(ka, qb[cb][kc], S[cb]);
+          for (int kc = 0; kc < NKC; ++kc)
+            Sn[cb] = mfma32(to.rowop(Kt, (kb + 1) * 32, kc), qb[cb][kc], Sn[cb]);
+        }
       }
       // Mask: key j (within the KV range) visible to query i iff j < kv_len and, causal,
       // j - i <= mask_offset.
@@ -173,7 +220,7 @@ void fwd_kernel(FwdArgs a) {
         float mx = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[cb][r]);
-        mx = fmaxf(mx, wave_xor32(mx)) * c;
+        mx = pair_max(mx) * c;
         if (m[cb] == -INFINITY) {
           m[cb] = mx;  // nothing accumulated yet: no rescale needed
           raise[cb] = false;
@@ -223,20 +270,23 @@ void fwd_kernel(FwdArgs a) {
         }
     }
 
-    wait_vmem();
+    // The next tile must have landed (with three slots its copy is older than the one
+    // just issued, which may stay in flight).
+    if (NBUF == 3 && nx2.valid)
+      wait_vmem_le<COPY_INSTS>();
+    else
+      wait_vmem();
     __syncthreads();
-    buf ^= 1;
-    s = ns;
-    t = ntile;
-    nt = nnt;
-    sg = nsg;
-    have = next;
+    buf = buf == NBUF - 1 ? 0 : buf + 1;
+    cur = nx1;
+    nx1 = nx2;
+    nx2 = nx2.next(a.segs, seg_end, it.q_off, it.q_rows);
   }
 
   // Epilogue: O = acc / l, LSE = (m + log2 l) ln 2; no visible key -> O = 0, LSE = -inf.
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
-    const float lt = l[cb] + wave_xor32(l[cb]);
+    const float lt = pair_sum(l[cb]);
     if (!valid[cb]) continue;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float lse = lt > 0.f ? (m[cb] + __log2f(lt)) * kLn2 : -INFINITY;
