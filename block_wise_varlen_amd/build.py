@@ -20,6 +20,8 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     # No packed fp32 instructions anywhere in the device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs; accumulators that live in AGPRs are placed there explicitly.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -353,14 +353,16 @@ int fcp_block_attn_bwd(const fcp_dims_t* dims, const void* q, const void* k, con
                      ws_bytes, stream, &P);
     if (st != FCP_OK || n_pairs == 0) return st;
     const fcp::Shape& s = P.shape;
-    float* delta = reinterpret_cast<float*>(static_cast<char*>(ws) + P.off_delta);
+    float* stats = reinterpret_cast<float*>(static_cast<char*>(ws) + P.off_delta);
     fcp::DeltaArgs da{};
     da.o = static_cast<const uint16_t*>(o);
     da.dout = static_cast<const uint16_t*>(dout);
+    da.lse = lse;
     da.rows = at<fcp::RowItem>(ws, P.off_rows);
     da.n_rows = P.n_rows;
     da.hq = s.hq;
-    da.delta = delta;
+    da.stats = stats;
+    da.q_rows = dims->q_rows;
     hipError_t e =
         timed(FCP_KERNEL_DELTA, stream, [&] { return fcp::launch_delta(da, s.d, stream); });
     if (e != hipSuccess) return hip_err(e, "delta launch");
@@ -369,8 +371,8 @@ int fcp_block_attn_bwd(const fcp_dims_t* dims, const void* q, const void* k, con
     a.k = static_cast<const uint16_t*>(k);
     a.v = static_cast<const uint16_t*>(v);
     a.dout = static_cast<const uint16_t*>(dout);
-    a.lse = lse;
-    a.delta = delta;
+    a.stats = stats;
+    a.q_rows = dims->q_rows;
     a.qitems = at<fcp::QItem>(ws, P.off_qitems);
     a.segs = at<fcp::KvSeg>(ws, P.off_segs);
     a.kvitems = at<fcp::KvItem>(ws, P.off_kvitems);

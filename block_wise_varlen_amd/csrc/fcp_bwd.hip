@@ -27,6 +27,7 @@
 namespace fcp {
 namespace {
 
+
 // ---------------------------------------------------------------------------------
 // dQ kernel
 // ---------------------------------------------------------------------------------
@@ -80,9 +81,11 @@ void dq_kernel(BwdArgs a) {
                              : zero_bf16x8();
     }
     // Rows with LSE = -inf (or padding rows) get P = 0 through an infinite shift.
-    const float L = valid[cb] ? a.lse[row * a.hq + head[cb]] : -INFINITY;
-    lse2[cb] = L == -INFINITY ? INFINITY : L * kLog2e;
-    dlt[cb] = valid[cb] ? a.delta[row * a.hq + head[cb]] : 0.f;
+    const f32x2_t st = valid[cb] ? *reinterpret_cast<const f32x2_t*>(
+                                       a.stats + 2 * (head[cb] * a.q_rows + row))
+                                 : f32x2_t{INFINITY, 0.f};
+    lse2[cb] = st[0];
+    dlt[cb] = st[1];
   }
 
   f32x16_t acc[CB][NDB];
@@ -95,7 +98,7 @@ void dq_kernel(BwdArgs a) {
   int s = it.seg_begin, t = 0, nt = 0;
   KvSeg sg{};
   for (; s < seg_end; ++s) {
-    sg = a.segs[s];
+    sg = load_uniform(a.segs, s);
     nt = seg_tiles(sg, it.q_off, it.q_rows);
     if (nt > 0) break;
   }
@@ -117,7 +120,7 @@ void dq_kernel(BwdArgs a) {
     if (ntile >= nnt) {
       ntile = 0;
       for (++ns; ns < seg_end; ++ns) {
-        nsg = a.segs[ns];
+        nsg = load_uniform(a.segs, ns);
         nnt = seg_tiles(nsg, it.q_off, it.q_rows);
         if (nnt > 0) break;
       }
@@ -180,7 +183,7 @@ void dq_kernel(BwdArgs a) {
     }
 
     wait_vmem();
-    __syncthreads();
+    lds_barrier();
     buf ^= 1;
     s = ns;
     t = ntile;
@@ -211,27 +214,79 @@ void dq_kernel(BwdArgs a) {
 // dK / dV kernel
 // ---------------------------------------------------------------------------------
 
-constexpr int kQRows = kQTileBwd;  // query rows per streamed tile (two 32-row blocks)
-constexpr int kDkdvWaves = kKvTileBwd / 32;
+constexpr int kDkdvWaves = kKvTileBwd / 32;  // 4: one wave per SIMD, 32 keys each
+constexpr int kDkdvRing = 5;                   // Q-tile ring depth
+static_assert(kQTileBwd == 32, "one 32-row MFMA block per streamed Q tile");
 
 // First query of segment `s` that sees any key of the item (causal), else 0.
 __device__ __forceinline__ int first_query(const QSeg& s, int key_off) {
   return (s.flags & 1) ? max(0, key_off - s.mask_offset) : 0;
 }
 
-// 8 waves (two per SIMD), each owning 32 keys as MFMA columns. K^T stays in registers;
-// the item's V block stays in LDS for the whole item and feeds dP = dO V^T.
+// Position in the (Q segment, 32-row Q tile, query head) sequence of one dK/dV item,
+// walked backwards over segments and tiles (heads innermost, ascending). Causally, every
+// KV item of a sequence then starts on the same last Q tile and they stream in step, so
+// concurrent workgroups share each Q / dO tile in L2; walking forwards, each would start
+// at its own diagonal and re-read Q from HBM.
+struct StepCursor {
+  QSeg sg;
+  int s, i0, lo, h;  // lo: first visible query of segment s
+  bool valid;
+  // Last tile of the last segment at or before `s_last` with a visible query.
+  __device__ static StepCursor last(const QSeg* qsegs, int s_first, int s_last, int key_off,
+                                    int h_first) {
+    StepCursor c{};
+    c.valid = false;
+    c.h = h_first;
+    for (c.s = s_last; c.s >= s_first; --c.s) {
+      c.sg = load_uniform(qsegs, c.s);
+      c.lo = first_query(c.sg, key_off);
+      if (c.lo < c.sg.q_len) {
+        c.i0 = c.lo + (c.sg.q_len - 1 - c.lo) / kQTileBwd * kQTileBwd;
+        c.valid = true;
+        break;
+      }
+    }
+    return c;
+  }
+  __device__ StepCursor next(const QSeg* qsegs, int s_first, int key_off, int h_first,
+                             int h_end) const {
+    if (!valid) return *this;
+    StepCursor c = *this;
+    if (++c.h < h_end) return c;
+    c.h = h_first;
+    c.i0 -= kQTileBwd;
+    if (c.i0 >= c.lo) return c;
+    return last(qsegs, s_first, s - 1, key_off, h_first);
+  }
+};
+
+// 4 waves (one per SIMD), each owning 32 keys as MFMA columns. The wave's K^T and V^T
+// (B operands of S = Q K^T and dP = dO V^T) stay in registers, its dK/dV accumulators in
+// the accumulation registers. Q tiles of 32 rows (with their dO rows and the rows'
+// base-2 LSE and Delta) stream through a 5-deep LDS ring with one barrier per tile.
+// The loop is software-pipelined over tiles: region t interleaves
+//   * the 16 MFMAs of S and dP for tile t + 1 (row reads of its Q and dO),
+//   * the 16 dV^T += dO^T P / dK^T += Q^T dS MFMAs of tile t - 1 (transpose reads),
+//   * the VALU work of tile t: P = exp2(S c - L2), dS = P (dP - Delta), bf16 packing,
+// so the matrix pipe, the VALU and LDS all stay busy from one wave. Ring slots live in
+// region t: t - 1, t, t + 1; t + 2 is landing and t + 3 is issued at the barrier before
+// region t into the slot of t - 2.
 template <int D>
-__global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void dkdv_kernel(BwdArgs a) {
   constexpr int NKC = D / 16;
   constexpr int NDB = D / 32;
   constexpr int NW = kDkdvWaves;
-  __shared__ __attribute__((aligned(16))) u16 sV[kKvTileBwd * D];
-  __shared__ __attribute__((aligned(16))) u16 sQ[2][kQRows * D];
-  __shared__ __attribute__((aligned(16))) u16 sG[2][kQRows * D];
-  __shared__ __attribute__((aligned(16))) float sL[2][kQRows];
-  __shared__ __attribute__((aligned(16))) float sD[2][kQRows];
+  constexpr int QR = kQTileBwd;
+  constexpr int NB = kDkdvRing;
+  // Loads per wave per tile: Q and dO rows, then one stats load.
+  constexpr int LOADS = 2 * tile_copy_insts<D, QR, NW>() + 1;
+  __shared__ __attribute__((aligned(16))) u16 sQ[NB][QR * D];
+  __shared__ __attribute__((aligned(16))) u16 sG[NB][QR * D];
+  // Per ring slot and wave: (L2, Delta) of the tile's rows 0..31, interleaved, in the
+  // first 64 of 256 floats (the load writes 16 bytes for each of the 64 lanes).
+  __shared__ __attribute__((aligned(16))) float sSt[NB][NW][256];
 
   const int item_idx = blockIdx.x / a.hkv;
   const int kvh = blockIdx.x - item_idx * a.hkv;
@@ -241,140 +296,181 @@ void dkdv_kernel(BwdArgs a) {
   const int64_t kv_stride = (int64_t)a.hkv * D;
   const int64_t q_stride = (int64_t)a.hq * D;
   const float c = a.scale_log2;
-
   const TileOffsets<D> to(lane);
-  // This lane's key column; K^T as B operand (k-slots d = 16*kc + 8*hi + 0..7).
-  const int key = wave * 32 + l32;  // within the item
+
+  // This lane's key column; K^T and V^T as B operands (k-slots d = 16*kc + 8*hi + 0..7).
+  const int key = wave * 32 + l32;
   const bool kvalid = key < it.kv_rows;
-  const int jkey = it.key_off + key;  // within the interval
-  bf16x8_t kb[NKC];
+  const int jkey = it.key_off + key;
+  bf16x8_t kb[NKC], vb[NKC];
   {
     const int64_t off = (int64_t)(it.kv_row0 + key) * kv_stride + (int64_t)kvh * D;
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc)
+    for (int kc = 0; kc < NKC; ++kc) {
       kb[kc] = kvalid ? *reinterpret_cast<const bf16x8_t*>(a.k + off + 16 * kc + 8 * hi)
                       : zero_bf16x8();
+      vb[kc] = kvalid ? *reinterpret_cast<const bf16x8_t*>(a.v + off + 16 * kc + 8 * hi)
+                      : zero_bf16x8();
+    }
   }
-  tile_copy_async<D, kKvTileBwd, NW>(a.v, it.kv_row0, it.kv_rows, kv_stride, (int64_t)kvh * D,
-                                     sV, wave, lane);
   f32x16_t dk[NDB], dv[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = zero16();
 
-  // Iteration space: segments x 64-row Q tiles (from each segment's first visible
-  // query) x query heads of the group.
   const int seg_end = it.seg_begin + it.seg_count;
   const int G = a.group;
   const int h_first = it.heads & 0xffff, h_end = h_first + (it.heads >> 16);
-  int s = it.seg_begin, i0 = 0, h = h_first;
-  QSeg sg{};
-  for (; s < seg_end; ++s) {
-    sg = a.qsegs[s];
-    i0 = first_query(sg, it.key_off);
-    if (i0 < sg.q_len) break;
-  }
-  bool have = s < seg_end;
-  float stat = 0.f;  // tid < 64: LSE (base 2) of row tid; 64 <= tid < 128: Delta
-  auto load_tile = [&](const QSeg& q, int r0, int head, int b) {
+  auto advance = [&](const StepCursor& x) {
+    return x.next(a.qsegs, it.seg_begin, it.key_off, h_first, h_end);
+  };
+  auto load = [&](const StepCursor& x, int b) {
+    const int head = kvh * G + x.h;
     const int64_t col = (int64_t)head * D;
-    tile_copy_async<D, kQRows, NW>(a.q, (int64_t)q.q_start + r0, q.q_len - r0, q_stride, col,
-                                   sQ[b], wave, lane);
-    tile_copy_async<D, kQRows, NW>(a.dout, (int64_t)q.q_start + r0, q.q_len - r0, q_stride, col,
-                                   sG[b], wave, lane);
-    if (tid < 2 * kQRows) {
-      const int r = tid & (kQRows - 1);
-      const bool ok = r0 + r < q.q_len;
-      const int64_t row = (int64_t)q.q_start + r0 + r;
-      if (tid < kQRows) {
-        const float L = ok ? a.lse[row * a.hq + head] : -INFINITY;
-        stat = L == -INFINITY ? INFINITY : L * kLog2e;
-      } else {
-        stat = ok ? a.delta[row * a.hq + head] : 0.f;
-      }
-    }
+    const int64_t r0 = (int64_t)x.sg.q_start + x.i0;
+    tile_copy_async<D, QR, NW>(a.q, r0, x.sg.q_len - x.i0, q_stride, col, sQ[b], wave, lane);
+    tile_copy_async<D, QR, NW>(a.dout, r0, x.sg.q_len - x.i0, q_stride, col, sG[b], wave, lane);
+    // (L2, Delta) of the tile's 32 rows: 256 contiguous bytes, one 16-byte load per lane
+    // for lanes 0..15 (one copy per wave, so every wave counts the same loads); rows past
+    // the range and lanes past 15 read as zero.
+    const uint32_t nbytes = (uint32_t)(min(x.sg.q_len - x.i0, QR) * 8);
+    dma16(buffer_rsrc(a.stats + 2 * (head * a.q_rows + r0), nbytes),
+          lds_addr(&sSt[b][__builtin_amdgcn_readfirstlane(wave)][0]),
+          lane < 16 ? lane * 16 : nbytes);
   };
-  auto store_stats = [&](int b) {
-    if (tid < kQRows)
-      sL[b][tid] = stat;
-    else if (tid < 2 * kQRows)
-      sD[b][tid - kQRows] = stat;
-  };
-  if (have) {
-    load_tile(sg, i0, kvh * G + h_first, 0);
-    store_stats(0);
-  }
+
+  // Cursors of tiles t + 1, t + 2, t + 3 at region t (tile t's is `cur`).
+  StepCursor cur = StepCursor::last(a.qsegs, it.seg_begin, seg_end - 1, it.key_off, h_first);
+  StepCursor n1 = advance(cur), n2 = advance(n1), n3 = advance(n2);
+  if (cur.valid) load(cur, 0);
+  if (n1.valid) load(n1, 1);
+  if (n2.valid) load(n2, 2);
+  // Tiles 0..2 and the K^T / V^T registers have landed after a full wait, which also
+  // tells the compiler that no load of its own is still pending in the loop.
   wait_vmem();
   __syncthreads();
-  int buf = 0;
+  if (n3.valid) load(n3, 3);
 
-  while (have) {
-    int ns = s, ni0 = i0, nh = h + 1;
-    QSeg nsg = sg;
-    if (nh == h_end) {
-      nh = h_first;
-      ni0 = i0 + kQRows;
-      if (ni0 >= sg.q_len) {
-        for (++ns; ns < seg_end; ++ns) {
-          nsg = a.qsegs[ns];
-          ni0 = first_query(nsg, it.key_off);
-          if (ni0 < nsg.q_len) break;
+  auto next_slot = [](int b) { return b == NB - 1 ? 0 : b + 1; };
+  // S and dP of tile t (computed in region t - 1), as MFMA results (rows = queries).
+  f32x16_t S = zero16(), dP = zero16();
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) {
+    S = mfma32(to.rowop(sQ[0], 0, kc), kb[kc], S);
+    dP = mfma32(to.rowop(sG[0], 0, kc), vb[kc], dP);
+  }
+  // P and dS (bf16 B operands) of tile t - 1 and its slot. Before the first tile they
+  // are zeros applied to slot 0 (finite data).
+  bf16x8_t pp[2], sp[2];
+  pp[0] = pp[1] = sp[0] = sp[1] = zero_bf16x8();
+  int pbuf = 0, buf = 0;
+
+  while (cur.valid) {
+    const int nbuf = next_slot(buf);
+    // (L2, Delta) of this lane's rows 8 g + 4 hi + e of tile t.
+    f32x4_t st[4][2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float* sp4 = &sSt[buf][wave][16 * g + 8 * hi];
+      st[g][0] = *reinterpret_cast<const f32x4_t*>(sp4);
+      st[g][1] = *reinterpret_cast<const f32x4_t*>(sp4 + 4);
+    }
+    // Causal: query i (within the segment) sees key jkey iff i >= jkey - mask_offset;
+    // rows past the range see nothing. Only tiles on the diagonal or a ragged end mask.
+    {
+      const QSeg sg = cur.sg;
+      const bool causal = sg.flags & 1;
+      const int rows_left = sg.q_len - cur.i0;
+      if ((causal && it.key_off + kKvTileBwd - 1 - sg.mask_offset > cur.i0) || rows_left < QR) {
+        const int lo = causal ? jkey - sg.mask_offset - cur.i0 : -QR;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (row < lo || row >= rows_left) S[r] = -INFINITY;
         }
       }
     }
-    const bool next = ns < seg_end;
-    if (next) load_tile(nsg, ni0, kvh * G + nh, buf ^ 1);
-
-    const u16* Qt = sQ[buf];
-    const u16* Gt = sG[buf];
-    const bool causal = sg.flags & 1;
-    // Causal: query i (within the segment) sees this lane's key iff i >= jkey - offset.
-    const int thr = jkey - sg.mask_offset - i0;  // tile row index threshold
-    const bool need_mask = causal && (it.key_off + kKvTileBwd - 1 - sg.mask_offset > i0);
-#pragma unroll 1
-    for (int rb = 0; rb < 2; ++rb) {
-      // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys.
-      f32x16_t S = zero16(), dP = zero16();
+    // ---- region t. Operand reads run PF MFMAs ahead of their use (LDS latency).
+    constexpr int NM = 2 * NKC;  // MFMAs per stream (S/dP of t + 1; dV/dK of t - 1)
+#ifndef FCP_DKDV_PF
+#define FCP_DKDV_PF 2
+#endif
+    constexpr int PF = FCP_DKDV_PF;
+    static_assert(NM <= 16 && 4 * NDB == NM, "stream lengths");
+    const u16* Qn = sQ[nbuf];
+    const u16* Gn = sG[nbuf];
+    auto next_op = [&](int n) { return to.rowop((n & 1) ? Gn : Qn, 0, n >> 1); };
+    auto prev_op = [&](int n) {
+      return to.trA((n & 1) ? sQ[pbuf] : sG[pbuf], 16 * ((n >> 1) & 1), (n >> 2) * 32);
+    };
+    bf16x8_t an[NM], ap[NM];
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        S = mfma32(to.rowop(Qt, rb * 32, kc), kb[kc], S);
-        dP = mfma32(to.rowop(Gt, rb * 32, kc), to.rowop(sV, wave * 32, kc), dP);
-      }
-      float p[16], ds[16];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int r0 = rb * 32 + 8 * g + 4 * hi;
-        const f32x4_t L4 = *reinterpret_cast<const f32x4_t*>(&sL[buf][r0]);
-        const f32x4_t D4 = *reinterpret_cast<const f32x4_t*>(&sD[buf][r0]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float pr = __builtin_amdgcn_exp2f(fmaf(S[r], c, -L4[e]));
-          if (need_mask && r0 + e < thr) pr = 0.f;
-          p[r] = pr;
-          ds[r] = pr * (dP[r] - D4[e]);
-        }
-      }
-      const bf16x8_t pb0 = to_bf16x8(p), pb1 = to_bf16x8(p + 8);
-      const bf16x8_t sb0 = to_bf16x8(ds), sb1 = to_bf16x8(ds + 8);
-      // dV^T += dO^T P and dK^T += Q^T dS over this block's 32 queries.
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        dv[db] = mfma32(to.trA(Gt, rb * 32, db * 32), pb0, dv[db]);
-        dv[db] = mfma32(to.trA(Gt, rb * 32 + 16, db * 32), pb1, dv[db]);
-        dk[db] = mfma32(to.trA(Qt, rb * 32, db * 32), sb0, dk[db]);
-        dk[db] = mfma32(to.trA(Qt, rb * 32 + 16, db * 32), sb1, dk[db]);
-      }
+    for (int i = 0; i < PF; ++i) {
+      an[i] = next_op(i);
+      ap[i] = prev_op(i);
     }
+    f32x16_t Sn = zero16(), dPn = zero16();
+    float p[16], ds[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i < NM) {
+        if (i + PF < NM) {
+          an[i + PF] = next_op(i + PF);
+          ap[i + PF] = prev_op(i + PF);
+        }
+        if (i & 1)
+          dPn = mfma32(an[i], vb[i >> 1], dPn);
+        else
+          Sn = mfma32(an[i], kb[i >> 1], Sn);
+        if (i & 1)
+          mfma32_agpr(dk[i >> 2], ap[i], sp[(i >> 1) & 1]);
+        else
+          mfma32_agpr(dv[i >> 2], ap[i], pp[(i >> 1) & 1]);
+      }
+      const int g = i >> 2, e = i & 3;
+      const float L2 = st[g][e >> 1][2 * (e & 1)];
+      const float Dl = st[g][e >> 1][2 * (e & 1) + 1];
+      p[i] = __builtin_amdgcn_exp2f(fmaf(S[i], c, -L2));
+      ds[i] = p[i] * (dP[i] - Dl);
+    }
+    const bf16x8_t pc0 = to_bf16x8(p), pc1 = to_bf16x8(p + 8);
+    const bf16x8_t sc0 = to_bf16x8(ds), sc1 = to_bf16x8(ds + 8);
+    // Keep the conversions in this region rather than sunk past the barrier below.
+    asm volatile("" ::"v"(pc0), "v"(pc1), "v"(sc0), "v"(sc1));
+    pp[0] = pc0;
+    pp[1] = pc1;
+    sp[0] = sc0;
+    sp[1] = sc1;
+    S = Sn;
+    dP = dPn;
+    pbuf = buf;
+    buf = nbuf;
 
-    if (next) store_stats(buf ^ 1);
-    wait_vmem();
-    __syncthreads();
-    buf ^= 1;
-    s = ns;
-    i0 = ni0;
-    h = nh;
-    sg = nsg;
-    have = next;
+    // Barrier before region t + 1: tile t + 2 must have landed (tile t + 3 may still be
+    // in flight), and every wave must be done with the slot of tile t - 1 (read above)
+    // before tile t + 4 is issued into it.
+    if (n3.valid)
+      wait_vmem_le<LOADS>();
+    else
+      wait_vmem();
+    lds_barrier();
+    cur = n1;
+    n1 = n2;
+    n2 = n3;
+    n3 = advance(n3);
+    if (n3.valid) load(n3, (pbuf + NB - 1) % NB);  // the slot of tile t - 1
+  }
+  // dV/dK of the last tile.
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      mfma32_agpr(dv[db], to.trA(sG[pbuf], 16 * half, db * 32), pp[half]);
+      mfma32_agpr(dk[db], to.trA(sQ[pbuf], 16 * half, db * 32), sp[half]);
+    }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    agpr_settle(dk[db]);
+    agpr_settle(dv[db]);
   }
 
   if (!kvalid) return;

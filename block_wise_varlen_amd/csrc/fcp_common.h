@@ -21,6 +21,7 @@ typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
 typedef uint32_t u32x4_t __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 typedef uint32_t u32x2_t __attribute__((__vector_size__(2 * sizeof(uint32_t))));
 typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
+typedef float f32x2_t __attribute__((__vector_size__(2 * sizeof(float))));
 typedef uint16_t u16;
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -28,6 +29,37 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// acc += a * b with the accumulator held in accumulation registers (AGPRs), for
+// long-lived accumulators of kernels that run one wave per SIMD (512 registers, of which
+// only 256 are addressable by VALU instructions). The other MFMAs are compiled in VGPR
+// form (-amdgpu-mfma-vgpr-form), so the compiler never shuffles these accumulators. The
+// two leading wait states cover a VALU write of a or b just before; a run of these
+// MFMAs on one accumulator needs none in between (same-size dependent accumulation).
+// Reading the accumulator with VALU instructions afterwards needs agpr_settle().
+__device__ __forceinline__ void mfma32_agpr(f32x16_t& acc, bf16x8_t a, bf16x8_t b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Wait states after the last mfma32_agpr on `acc` before its registers are read (a
+// 16-pass MFMA result needs 18; 40 are given).
+__device__ __forceinline__ void agpr_settle(f32x16_t& acc) {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+a"(acc));
+}
+
+// acc (VGPRs) = a * b, and acc += a * b, with the B operand read from accumulation
+// registers: a stationary operand parked there leaves the VGPRs to streamed operands.
+// As these are opaque to the compiler's hazard tracking, VALU reads of acc must follow
+// vgpr_settle().
+__device__ __forceinline__ void mfma32_ab_first(f32x16_t& acc, bf16x8_t a, const bf16x8_t& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma32_ab(f32x16_t& acc, bf16x8_t a, const bf16x8_t& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void vgpr_settle(f32x16_t& x, f32x16_t& y) {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+v"(x), "+v"(y));
 }
 
 __device__ __forceinline__ f32x16_t zero16() {
@@ -89,19 +121,56 @@ __device__ __forceinline__ u32x2_t lds_tr4(const u16* p) {
 // ---- LDS tiles ---------------------------------------------------------------------
 //
 // A tile is ROWS x D bf16 stored row-major without padding, each 16-byte chunk c of row
-// r at chunk position c ^ swz(r). With swz(r) = 2 (r % 4) + (r / 4) % 2 both read
-// patterns below touch 32 distinct banks per 128-byte LDS cycle: 16-byte row reads of 8
-// consecutive rows at one chunk, and transpose reads of 4 consecutive rows x 2 chunks.
-// swz(r + 8) == swz(r).
-__device__ __forceinline__ int swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+// r at chunk position c ^ swz<D>(r). gfx950 LDS has 64 four-byte banks and serves a
+// 16-byte read for 16 lanes per cycle, an 8-byte read for 32. The swizzle makes both
+// read patterns below conflict-free:
+//  * 16-byte row reads of 16 consecutive rows at one chunk (D = 128: one row spans all
+//    64 banks, so the 16 rows need 16 distinct chunk positions; D = 64: two rows share a
+//    bank line, so the 8 rows of each parity need 8 distinct positions);
+//  * transpose reads of 4 consecutive rows x 4 chunks (rows at distinct chunk quads).
+// swz<D>(r) depends on r % 16 only.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(D == 64 || D == 128, "head dim");
+  if constexpr (D == 128)
+    return 4 * (r & 3) + ((r >> 2) & 3);
+  else
+    return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+
+// Buffer resource over `num_bytes` bytes at `base` (raw, no stride): loads at offsets
+// past num_bytes return zero.
+__device__ __forceinline__ u32x4_t buffer_rsrc(const void* base, uint32_t num_bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, num_bytes, 0x00020000u};
+}
+
+// LDS address (byte offset in the workgroup's LDS) of a __shared__ object.
+template <class T>
+__device__ __forceinline__ uint32_t lds_addr(const T* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) T*)p;
+}
+
+// Direct global -> LDS load: lane l's 16 bytes at rsrc + voff land at LDS lds + 16 l
+// (buffer_load_dwordx4 ... lds; M0 holds the wave-uniform LDS address). Issued through
+// inline assembly on purpose: the compiler then does not see an LDS write in flight and
+// does not wait for it (vmcnt(0)) before every later LDS read -- which would serialise
+// each prefetch with the compute it should overlap. The kernels order these copies
+// themselves: s_waitcnt vmcnt (loads complete in issue order) + barrier before the data
+// is read, and a barrier after the last read of a slot before it is refilled.
+__device__ __forceinline__ void dma16(const u32x4_t& rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
 
 // Asynchronous global -> LDS copy of rows [row0, row0 + ROWS) of a bf16 tensor whose rows
 // are `stride` elements apart, starting at column `col0` (one head), into `tile`. Rows at
 // or past `valid` read as zero (buffer range check). Every wave of the NW-wave
-// workgroup issues its share; the data is in LDS after s_waitcnt vmcnt(0) + barrier.
-// buffer_load_dwordx4 ... lds writes lane l's 16 bytes to M0 + 16 l, so each wave
-// instruction fills 1 KB of the tile and the lane picks the global chunk that belongs at
-// its LDS position.
+// workgroup issues its share (tile_copy_insts loads); the data may be read after this
+// wave's s_waitcnt vmcnt and a barrier. Each wave instruction fills 1 KB of the tile and
+// the lane picks the global chunk that belongs at its LDS position.
 template <int D, int ROWS, int NW = 4>
 __device__ __forceinline__ void tile_copy_async(const u16* src, int64_t row0, int valid,
                                                 int64_t stride, int64_t col0, u16* tile,
@@ -113,54 +182,76 @@ __device__ __forceinline__ void tile_copy_async(const u16* src, int64_t row0, in
   static_assert(NI % NW == 0, "tile must split over the waves");
   const int vrows = valid < 0 ? 0 : (valid > ROWS ? ROWS : valid);
   const uint32_t nbytes = vrows > 0 ? (uint32_t)(((int64_t)(vrows - 1) * stride + D) * 2) : 0u;
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(src + row0 * stride + col0), (short)0, (int)nbytes, 0x00020000);
+  const u32x4_t rsrc = buffer_rsrc(src + row0 * stride + col0, nbytes);
+  const int w = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
-    const int ins = wave * PER_WAVE + i;
+    const int ins = w * PER_WAVE + i;
     const int r = ins * RPI + lane / CPR;
-    const int c = (lane % CPR) ^ swz(r);
-    const int voff = (int)(((int64_t)r * stride + c * 8) * 2);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsrc, (__attribute__((address_space(3))) void*)(tile + ins * 512), 16, voff, 0, 0, 0);
+    const int c = (lane % CPR) ^ swz<D>(r);
+    const uint32_t voff = (uint32_t)(((int64_t)r * stride + c * 8) * 2);
+    dma16(rsrc, lds_addr(tile + ins * 512), voff);
   }
 }
 
 // MFMA operand reads from a swizzled tile, with the per-lane LDS element offsets shared
-// by every tile a lane reads (6 registers in all).
+// by every tile a lane reads (D / 8 registers).
 //  * rowop(tile, row0, kc): lane row/column l % 32 taken from tile row row0 + l % 32,
-//    slots 16 kc + 8 (l / 32) + 0..7 along the row (row0 % 8 == 0): K for S^T = K Q^T,
-//    Q or dO for S = Q K^T. It sits at row0 * D + row[kc % 4] + 64 (kc / 4).
+//    slots 16 kc + 8 (l / 32) + 0..7 along the row (row0 % 16 == 0): K for S^T = K Q^T,
+//    Q or dO for S = Q K^T.
 //  * trA(tile, k16, c32): the A operand (32 x 16) of a contraction over the tile's ROW
 //    index: result rows are tile columns c32 .. c32 + 31, slot s of lane half h is tile
 //    row k16 + 8 (s / 4) + 4 h + s % 4 -- the row order of a 32x32 MFMA result, so the
 //    B operand can come straight from result registers. Two ds_read_b64_tr_b16 of 4 rows
-//    each, at k16 * D + tr[(c32 / 32) % 2] + 64 (c32 / 64) and 8 D further
-//    (k16 % 16 == 0, c32 % 32 == 0).
+//    each, rows k16 + 0..7 and k16 + 8..15 (k16 % 16 == 0, c32 % 32 == 0).
 template <int D>
 struct TileOffsets {
-  int row[4];
-  int tr[2];
+  static constexpr int NKC = D / 16, NCB = D / 32;
+  int row[NKC];
+  int tr[2][NCB];
   __device__ explicit TileOffsets(int lane) {
-    const int r = lane & 31, s = swz(r), h = lane >> 5;
+    const int r = lane & 31, s = swz<D>(r), h = lane >> 5;
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) row[kc] = r * D + (((2 * kc + h) ^ s) << 3);
+    for (int kc = 0; kc < NKC; ++kc) row[kc] = r * D + (((2 * kc + h) ^ s) << 3);
     const int j = lane & 15, grp = lane >> 4;
-    const int tr_r = 4 * (grp >> 1) + (j >> 2);
     const int x = 2 * (grp & 1) + ((j & 3) >> 1);  // chunk within a 32-column block
 #pragma unroll
-    for (int odd = 0; odd < 2; ++odd)
-      tr[odd] = tr_r * D + (((4 * odd + x) ^ swz(tr_r)) << 3) + 4 * (j & 1);
+    for (int half = 0; half < 2; ++half) {
+      const int tr_r = 8 * half + 4 * (grp >> 1) + (j >> 2);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        tr[half][cb] = tr_r * D + (((4 * cb + x) ^ swz<D>(tr_r)) << 3) + 4 * (j & 1);
+    }
   }
   __device__ __forceinline__ bf16x8_t rowop(const u16* tile, int row0, int kc) const {
-    return *reinterpret_cast<const bf16x8_t*>(tile + row0 * D + row[kc & 3] + 64 * (kc >> 2));
+    return *reinterpret_cast<const bf16x8_t*>(tile + row0 * D + row[kc]);
   }
   __device__ __forceinline__ bf16x8_t trA(const u16* tile, int k16, int c32) const {
-    const u16* p = tile + k16 * D + tr[(c32 >> 5) & 1] + 64 * (c32 >> 6);
-    const u32x2_t lo = lds_tr4(p), hi = lds_tr4(p + 8 * D);
+    const u16* p = tile + k16 * D;
+    const u32x2_t lo = lds_tr4(p + tr[0][c32 >> 5]), hi = lds_tr4(p + tr[1][c32 >> 5]);
     return __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
   }
 };
+
+// Workgroup barrier for LDS tiles filled by dma16: waits for this wave's own LDS (and
+// scalar) operations, then s_barrier. Unlike __syncthreads, whose release fence also
+// waits for every outstanding global load (vmcnt(0)), it leaves prefetches in flight; the
+// callers wait for the copies a tile needs (wait_vmem / wait_vmem_le) before it. The
+// memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Element i of a work-list table (read-only for the kernel's lifetime), for a wave-
+// uniform i, through the scalar cache: a vector load would make the compiler wait for
+// every outstanding tile copy before using the value.
+template <class T>
+__device__ __forceinline__ T load_uniform(const T* table, int i) {
+  static_assert(sizeof(T) == sizeof(u32x4_t), "16-byte records");
+  const __attribute__((address_space(4))) u32x4_t* t =
+      (const __attribute__((address_space(4))) u32x4_t*)table;
+  return __builtin_bit_cast(T, t[__builtin_amdgcn_readfirstlane(i)]);
+}
 
 // Waits for this wave's outstanding vector-memory operations (the async tile copies).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }

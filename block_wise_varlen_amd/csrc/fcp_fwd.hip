@@ -27,6 +27,7 @@
 #include "fcp_kernels.h"
 #include "fcp_types.h"
 
+
 namespace fcp {
 namespace {
 
@@ -34,11 +35,7 @@ namespace {
 constexpr float kRescaleSlack = 8.0f;
 
 // Keys per K/V tile of the forward and depth of its LDS ring.
-#ifndef FCP_FWD_KT
-#define FCP_FWD_KT 128
-#endif
-constexpr int kFwdKt = FCP_FWD_KT;
-constexpr int kFwdBuf = kFwdKt == 64 ? 3 : 2;
+constexpr int kFwdKt = 128;
 
 // Number of kFwdKt-key tiles of segment `s` visible to queries [q_off, q_off + rows).
 __device__ __forceinline__ int seg_tiles(const KvSeg& s, int q_off, int rows) {
@@ -58,7 +55,7 @@ struct TileCursor {
     TileCursor c{};
     c.valid = false;
     for (c.s = s0; c.s < s_end; ++c.s) {
-      c.sg = segs[c.s];
+      c.sg = load_uniform(segs, c.s);
       c.nt = seg_tiles(c.sg, q_off, rows);
       if (c.nt > 0) {
         c.valid = true;
@@ -79,17 +76,19 @@ struct TileCursor {
   }
 };
 
+// Scheduling hints (LLVM AMDGPU sched_group_barrier masks).
+constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100;
+
 template <int D, bool FINAL, int CB>
 __global__ __launch_bounds__(64 * kColBlocksPerWG / CB)
 __attribute__((amdgpu_waves_per_eu(CB == 1 ? 2 : 1, CB == 1 ? 2 : 1)))
 void fwd_kernel(FwdArgs a) {
   constexpr int NW = kColBlocksPerWG / CB;  // waves per workgroup
-  constexpr int NKC = D / 16;   // k-chunks of the QK^T contraction
-  constexpr int NDB = D / 32;   // d-blocks of the output
-  constexpr int NBUF = kFwdBuf;  // tile ring depth
-  constexpr int COPY_INSTS = 2 * tile_copy_insts<D, kFwdKt, NW>();
-  __shared__ __attribute__((aligned(16))) u16 sK[NBUF][kFwdKt * D];
-  __shared__ __attribute__((aligned(16))) u16 sV[NBUF][kFwdKt * D];
+  constexpr int NKC = D / 16;               // k-chunks of the QK^T contraction
+  constexpr int NDB = D / 32;               // d-blocks of the output
+  constexpr int NKB = kFwdKt / 32;          // 32-key blocks per tile
+  __shared__ __attribute__((aligned(16))) u16 sK[2][kFwdKt * D];
+  __shared__ __attribute__((aligned(16))) u16 sV[2][kFwdKt * D];
 
   const int item_idx = blockIdx.x / a.n_hgroups;
   const int hg = blockIdx.x - item_idx * a.n_hgroups;
@@ -102,6 +101,8 @@ void fwd_kernel(FwdArgs a) {
   const int64_t kv_stride = (int64_t)a.hkv * D;
   const TileOffsets<D> to(lane);
 
+  // Column block cbg = wave * CB + cb covers tokens (cbg / hpw) * 32 + 0..31 of head
+  // head_base + cbg % hpw.
   int tok[CB], head[CB];
   bool valid[CB];
 #pragma unroll
@@ -135,11 +136,11 @@ void fwd_kernel(FwdArgs a) {
 
   const int seg_end = it.seg_begin + it.seg_count;
   const int64_t kv_col = (int64_t)kvh * D;
+  const float c = a.scale_log2;
   // Cursors over the flattened (segment, tile) sequence: the tile being computed and the
-  // two after it, whose copies are in flight.
+  // one after it.
   TileCursor cur = TileCursor::first(a.segs, it.seg_begin, seg_end, it.q_off, it.q_rows);
-  TileCursor nx1 = cur.next(a.segs, seg_end, it.q_off, it.q_rows);
-  TileCursor nx2 = nx1.next(a.segs, seg_end, it.q_off, it.q_rows);
+  TileCursor nx = cur.next(a.segs, seg_end, it.q_off, it.q_rows);
   auto copy = [&](const TileCursor& tc, int b) {
     const int j0n = tc.t * kFwdKt;
     tile_copy_async<D, kFwdKt, NW>(a.k, (int64_t)tc.sg.kv_start + j0n, tc.sg.kv_len - j0n,
@@ -147,63 +148,72 @@ void fwd_kernel(FwdArgs a) {
     tile_copy_async<D, kFwdKt, NW>(a.v, (int64_t)tc.sg.kv_start + j0n, tc.sg.kv_len - j0n,
                                    kv_stride, kv_col, sV[b], wave, lane);
   };
+
+  // Software pipeline over 32-key blocks. Step kb runs two regions:
+  //   A: the PV MFMAs of block kb - 1 | K operand reads for block kb + 1 | mask + row max
+  //      of block kb;
+  //   (rare branch: raise the running max, rescale the accumulator)
+  //   B: the QK^T MFMAs of block kb + 1 | V^T operand reads for block kb | exp2, row sum
+  //      and bf16 conversion of block kb.
+  // Each region interleaves the wave's MFMAs with its own VALU work and with LDS reads
+  // issued one region ahead of their use. The pipeline runs across tile boundaries; the
+  // first pending PV multiplies zeros, the last QK^T (past the final tile) is discarded.
+  f32x16_t S[CB];  // scores of the block whose softmax is next
+  bf16x8_t pb[CB][2], va[2 * NDB], kop[NKC];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    S[cb] = zero16();
+    pb[cb][0] = pb[cb][1] = zero_bf16x8();
+  }
+#pragma unroll
+  for (int i = 0; i < 2 * NDB; ++i) va[i] = zero_bf16x8();
+
   if (cur.valid) copy(cur, 0);
-  if (NBUF == 3 && nx1.valid) copy(nx1, 1);
-  if (NBUF == 3 && nx1.valid)
-    wait_vmem_le<COPY_INSTS>();
-  else
-    wait_vmem();
+  if (nx.valid) copy(nx, 1);
+  // Everything issued so far (Q^T, both tiles) is complete after a full wait, which also
+  // tells the compiler that no load of its own is still pending in the loop.
+  wait_vmem();
   __syncthreads();
+  if (cur.valid) {
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      const bf16x8_t kk = to.rowop(sK[0], 0, kc);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) S[cb] = mfma32(kk, qb[cb][kc], S[cb]);
+    }
+  }
   int buf = 0;
-  const float c = a.scale_log2;
+  bool first_tile = true;
 
   while (cur.valid) {
-    // The ring slot after the in-flight ones was last read in the previous iteration,
-    // which every wave has left (barrier), so the next copy may overwrite it.
-    if (NBUF == 3) {
-      if (nx2.valid) copy(nx2, buf == 0 ? 2 : buf - 1);
-    } else {
-      if (nx1.valid) copy(nx1, buf ^ 1);
+    // Tile n + 1 goes into the slot of tile n - 1, whose last reads (the V^T operands of
+    // its final block) every wave has completed before this barrier.
+    if (!first_tile && nx.valid) {
+      lds_barrier();
+      copy(nx, buf ^ 1);
     }
     const KvSeg sg = cur.sg;
-    const int t = cur.t;
-
-    const u16* Kt = sK[buf];
-    const u16* Vt = sV[buf];
-    const int j0 = t * kFwdKt;
+    const int j0 = cur.t * kFwdKt;
     const bool causal = sg.flags & 1;
     const bool need_mask = (j0 + kFwdKt > sg.kv_len) ||
                            (causal && j0 + kFwdKt - 1 - it.q_off > sg.mask_offset);
-    // 32-key blocks, software-pipelined: the S^T = K Q^T MFMAs of block kb + 1 are issued
-    // before the softmax of block kb, so the matrix pipe works while the VALU does.
-    constexpr int NKB = kFwdKt / 32;
-    f32x16_t Sn[CB];
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      Sn[cb] = zero16();
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) Sn[cb] = mfma32(to.rowop(Kt, 0, kc), qb[cb][kc], Sn[cb]);
-    }
+    const u16* Kt = sK[buf];
+    const u16* Vt = sV[buf];
+    const u16* Kn = sK[buf ^ 1];
+
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      f32x16_t S[CB];
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) S[cb] = Sn[cb];
-      if (kb + 1 < NKB) {
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          Sn[cb] = zero16();
-#pragma unroll
-          for (int kc = 0; kc < NKC; ++kc)
-            Sn[cb] = mfma32(to.rowop(Kt, (kb + 1) * 32, kc), qb[cb][kc], Sn[cb]);
-        }
+      if (kb == NKB - 1 && nx.valid) {
+        // The next tile's K is read from here on.
+        wait_vmem();
+        lds_barrier();
       }
-      // Mask: key j (within the KV range) visible to query i iff j < kv_len and, causal,
-      // j - i <= mask_offset.
       if (need_mask) {
+        // Key j (within the KV range) visible to query i iff j < kv_len and, causal,
+        // j - i <= mask_offset. Only tiles on a diagonal or a ragged end take this branch.
+        const int jb = j0 + kb * 32;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-          const int jb = j0 + kb * 32;
           const int lim_c = sg.mask_offset + it.q_off + tok[cb] - jb;
           const int lim = causal ? min(sg.kv_len - jb - 1, lim_c) : sg.kv_len - jb - 1;
 #pragma unroll
@@ -211,32 +221,48 @@ void fwd_kernel(FwdArgs a) {
             if (8 * (r >> 2) + 4 * hi + (r & 3) > lim) S[cb][r] = -INFINITY;
         }
       }
-      // Online softmax in base 2 with the scale folded into the exponent; the running
-      // max m is raised only when the block's max exceeds it by more than kRescaleSlack.
-      bool raise[CB];
-      float m_new[CB];
+      // ---- region A
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+            acc[cb][db] = mfma32(va[2 * db + half], pb[cb][half], acc[cb][db]);
+      {
+        const u16* kt = kb + 1 < NKB ? Kt : Kn;
+        const int kr = kb + 1 < NKB ? (kb + 1) * 32 : 0;
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) kop[kc] = to.rowop(kt, kr, kc);
+      }
+      bool raise[CB], any_raise = false;
+      float mx[CB];
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        float mx = -INFINITY;
+        // Online softmax in base 2 with the scale folded into the exponent; the running
+        // max is raised only when the block's max exceeds it by more than kRescaleSlack.
+        float x = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[cb][r]);
-        mx = pair_max(mx) * c;
-        if (m[cb] == -INFINITY) {
-          m[cb] = mx;  // nothing accumulated yet: no rescale needed
-          raise[cb] = false;
-        } else {
-          raise[cb] = mx > m[cb] + kRescaleSlack;
-        }
-        m_new[cb] = fmaxf(m[cb], mx);
+        for (int r = 0; r < 16; ++r) x = fmaxf(x, S[cb][r]);
+        mx[cb] = pair_max(x) * c;
+        raise[cb] = false;
+        if (m[cb] == -INFINITY)
+          m[cb] = mx[cb];  // nothing accumulated yet: no rescale needed
+        else
+          raise[cb] = mx[cb] > m[cb] + kRescaleSlack;
+        any_raise = any_raise || raise[cb];
       }
-      bool any_raise = false;
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) any_raise = any_raise || raise[cb];
+      for (int i = 0; i < 2 * NDB * CB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        if (i < NKC) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgValu, 3, 0);
+      }
       if (__any(any_raise)) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-          const float alpha = raise[cb] ? __builtin_amdgcn_exp2f(m[cb] - m_new[cb]) : 1.f;
-          m[cb] = raise[cb] ? m_new[cb] : m[cb];
+          const float alpha = raise[cb] ? __builtin_amdgcn_exp2f(m[cb] - mx[cb]) : 1.f;
+          m[cb] = raise[cb] ? mx[cb] : m[cb];
           l[cb] *= alpha;
 #pragma unroll
           for (int db = 0; db < NDB; ++db)
@@ -244,7 +270,19 @@ void fwd_kernel(FwdArgs a) {
             for (int r = 0; r < 16; ++r) acc[cb][db][r] *= alpha;
         }
       }
-      bf16x8_t pb[CB][2];
+      // ---- region B
+      f32x16_t Sn[CB];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) Sn[cb] = zero16();
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) Sn[cb] = mfma32(kop[kc], qb[cb][kc], Sn[cb]);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        va[2 * db] = to.trA(Vt, kb * 32, db * 32);
+        va[2 * db + 1] = to.trA(Vt, kb * 32 + 16, db * 32);
+      }
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const float m_use = (m[cb] == -INFINITY) ? 0.f : m[cb];
@@ -258,30 +296,29 @@ void fwd_kernel(FwdArgs a) {
         l[cb] += rs;
         pb[cb][0] = to_bf16x8(p);
         pb[cb][1] = to_bf16x8(p + 8);
+        S[cb] = Sn[cb];
       }
-      // O^T += V^T P^T over the block's 32 keys.
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const bf16x8_t va = to.trA(Vt, kb * 32 + 16 * half, db * 32);
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) acc[cb][db] = mfma32(va, pb[cb][half], acc[cb][db]);
-        }
+      for (int i = 0; i < NKC * CB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        if (i < 4 * NDB) __builtin_amdgcn_sched_group_barrier(kSgDsRead, (4 * NDB + NKC * CB - 1) / (NKC * CB), 0);
+        __builtin_amdgcn_sched_group_barrier(kSgValu, 6, 0);
+      }
     }
 
-    // The next tile must have landed (with three slots its copy is older than the one
-    // just issued, which may stay in flight).
-    if (NBUF == 3 && nx2.valid)
-      wait_vmem_le<COPY_INSTS>();
-    else
-      wait_vmem();
-    __syncthreads();
-    buf = buf == NBUF - 1 ? 0 : buf + 1;
-    cur = nx1;
-    nx1 = nx2;
-    nx2 = nx2.next(a.segs, seg_end, it.q_off, it.q_rows);
+    buf ^= 1;
+    first_tile = false;
+    cur = nx;
+    nx = nx.next(a.segs, seg_end, it.q_off, it.q_rows);
   }
+  // PV of the last block.
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        acc[cb][db] = mfma32(va[2 * db + half], pb[cb][half], acc[cb][db]);
 
   // Epilogue: O = acc / l, LSE = (m + log2 l) ln 2; no visible key -> O = 0, LSE = -inf.
 #pragma unroll
@@ -318,9 +355,12 @@ void fwd_kernel(FwdArgs a) {
 
 }  // namespace
 
-// Column blocks per wave of the launched forward: 1 (8 waves, two per SIMD, so one
-// wave's softmax overlaps the other's MFMAs) or 2 (4 waves, one per SIMD).
-constexpr int kFwdCB = 1;
+// Column blocks per wave of the launched forward: 2 (4 waves, one per SIMD, each K / V
+// operand read from LDS feeds two MFMAs) or 1 (8 waves, two per SIMD).
+#ifndef FCP_FWD_CB
+#define FCP_FWD_CB 1
+#endif
+constexpr int kFwdCB = FCP_FWD_CB;
 
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool final_out, hipStream_t stream) {
   if (a.n_items == 0) return hipSuccess;

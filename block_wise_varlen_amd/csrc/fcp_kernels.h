@@ -37,10 +37,12 @@ struct MergeArgs {
 struct DeltaArgs {
   const uint16_t* o;     // bf16 merged output
   const uint16_t* dout;  // bf16 upstream gradient
+  const float* lse;      // fp32 [q_rows, hq], natural log
   const RowItem* rows;
   int n_rows;
   int hq;
-  float* delta;  // fp32 [q_rows, hq]
+  float* stats;  // fp32 [hq, q_rows, 2]: LSE * log2(e) (+inf where LSE = -inf), Delta
+  int64_t q_rows;
 };
 
 struct BwdArgs {
@@ -48,8 +50,8 @@ struct BwdArgs {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dout;
-  const float* lse;    // fp32 [q_rows, hq], natural log
-  const float* delta;  // fp32 [q_rows, hq]
+  const float* stats;  // fp32 [hq, q_rows, 2] from the Delta kernel
+  int64_t q_rows;
   const QItem* qitems;
   const KvSeg* segs;
   const KvItem* kvitems;

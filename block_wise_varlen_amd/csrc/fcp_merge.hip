@@ -70,7 +70,10 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   }
 }
 
-// Delta_i = sum_d dO_i[d] * O_i[d] per (row, head), in fp32 from the bf16 tensors.
+// Delta_i = sum_d dO_i[d] * O_i[d] per (row, head), in fp32 from the bf16 tensors, stored
+// beside the row's LSE in base 2 (+inf for a row that sees no key, so exp2(x - L2) = 0),
+// head-major: the backward kernels read the pair with one 8-byte load per (row, head), and
+// the stats of a run of rows of one head are contiguous.
 template <int D>
 __global__ __launch_bounds__(256) void delta_kernel(DeltaArgs a) {
   constexpr int CPH = D / 8;  // 16-byte chunks per head
@@ -91,7 +94,13 @@ __global__ __launch_bounds__(256) void delta_kernel(DeltaArgs a) {
     }
 #pragma unroll
     for (int off = CPH / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-    if (e < total && (e % CPH) == 0) a.delta[(int64_t)it.q_row * a.hq + e / CPH] = s;
+    if (e < total && (e % CPH) == 0) {
+      const int h = e / CPH;
+      const float L = a.lse[(int64_t)it.q_row * a.hq + h];
+      const float L2 = L == -INFINITY ? INFINITY : L * kLog2e;
+      *reinterpret_cast<f32x2_t*>(a.stats + 2 * ((int64_t)h * a.q_rows + it.q_row)) =
+          f32x2_t{L2, s};
+    }
   }
 }
 

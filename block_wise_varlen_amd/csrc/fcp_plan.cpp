@@ -358,7 +358,7 @@ int make_plan(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t n_pairs, 
     P.n_reduce = (int)reduce.size();
     P.n_slots = n_slots;
     P.off_delta = align_up(P.blob.size());
-    P.off_partial = P.off_delta + align_up((size_t)dims->q_rows * s.hq * sizeof(float));
+    P.off_partial = P.off_delta + align_up((size_t)dims->q_rows * s.hq * 2 * sizeof(float));
     // Partial slots: dK then dV, each [slot][kv head][kKvTileBwd][D] fp32.
     P.ws_bytes = P.off_partial +
                  align_up(2 * (size_t)n_slots * s.hkv * kKvTileBwd * s.d * sizeof(float));

@@ -15,10 +15,10 @@ constexpr int kColBlock = 32;
 constexpr int kColBlocksPerWG = 8;
 // Keys per KV tile of the forward and dQ kernels.
 constexpr int kKvTile = 64;
-// Keys per workgroup tile of the dK/dV kernel (8 waves x 32 keys).
-constexpr int kKvTileBwd = 256;
+// Keys per workgroup tile of the dK/dV kernel (4 waves x 32 keys).
+constexpr int kKvTileBwd = 128;
 // Query rows per Q tile streamed by the dK/dV kernel.
-constexpr int kQTileBwd = 64;
+constexpr int kQTileBwd = 32;
 
 // One forward / dQ work item: a tile of up to `q_rows` consecutive query rows of one
 // Q range, for one group of query heads (the head group comes from the grid), against
