@@ -104,11 +104,10 @@ void dq_kernel(BwdArgs a) {
   }
   bool have = s < seg_end;
   const int64_t kv_col = (int64_t)kvh * D;
+  const TileCopy<D, kKvTile, NW> tcopy(kv_stride, wave, lane);
   if (have) {
-    tile_copy_async<D, kKvTile, NW>(a.k, sg.kv_start, sg.kv_len, kv_stride, kv_col, sK[0], wave,
-                                    lane);
-    tile_copy_async<D, kKvTile, NW>(a.v, sg.kv_start, sg.kv_len, kv_stride, kv_col, sV[0], wave,
-                                    lane);
+    tcopy(a.k, sg.kv_start, sg.kv_len, kv_col, sK[0]);
+    tcopy(a.v, sg.kv_start, sg.kv_len, kv_col, sV[0]);
     wait_vmem();
   }
   __syncthreads();
@@ -128,10 +127,8 @@ void dq_kernel(BwdArgs a) {
     const bool next = ns < seg_end;
     if (next) {
       const int j0n = ntile * kKvTile;
-      tile_copy_async<D, kKvTile, NW>(a.k, (int64_t)nsg.kv_start + j0n, nsg.kv_len - j0n,
-                                      kv_stride, kv_col, sK[buf ^ 1], wave, lane);
-      tile_copy_async<D, kKvTile, NW>(a.v, (int64_t)nsg.kv_start + j0n, nsg.kv_len - j0n,
-                                      kv_stride, kv_col, sV[buf ^ 1], wave, lane);
+      tcopy(a.k, (int64_t)nsg.kv_start + j0n, nsg.kv_len - j0n, kv_col, sK[buf ^ 1]);
+      tcopy(a.v, (int64_t)nsg.kv_start + j0n, nsg.kv_len - j0n, kv_col, sV[buf ^ 1]);
     }
 
     const u16* Kt = sK[buf];
@@ -323,19 +320,20 @@ void dkdv_kernel(BwdArgs a) {
   auto advance = [&](const StepCursor& x) {
     return x.next(a.qsegs, it.seg_begin, it.key_off, h_first, h_end);
   };
+  const TileCopy<D, QR, NW> tcopy(q_stride, wave, lane);
+  const uint32_t st_off = lane < 16 ? lane * 16 : 0x7fffffffu;  // lanes past 15: no data
   auto load = [&](const StepCursor& x, int b) {
     const int head = kvh * G + x.h;
     const int64_t col = (int64_t)head * D;
     const int64_t r0 = (int64_t)x.sg.q_start + x.i0;
-    tile_copy_async<D, QR, NW>(a.q, r0, x.sg.q_len - x.i0, q_stride, col, sQ[b], wave, lane);
-    tile_copy_async<D, QR, NW>(a.dout, r0, x.sg.q_len - x.i0, q_stride, col, sG[b], wave, lane);
+    tcopy(a.q, r0, x.sg.q_len - x.i0, col, sQ[b]);
+    tcopy(a.dout, r0, x.sg.q_len - x.i0, col, sG[b]);
     // (L2, Delta) of the tile's 32 rows: 256 contiguous bytes, one 16-byte load per lane
     // for lanes 0..15 (one copy per wave, so every wave counts the same loads); rows past
     // the range and lanes past 15 read as zero.
     const uint32_t nbytes = (uint32_t)(min(x.sg.q_len - x.i0, QR) * 8);
     dma16(buffer_rsrc(a.stats + 2 * (head * a.q_rows + r0), nbytes),
-          lds_addr(&sSt[b][__builtin_amdgcn_readfirstlane(wave)][0]),
-          lane < 16 ? lane * 16 : nbytes);
+          lds_addr(&sSt[b][__builtin_amdgcn_readfirstlane(wave)][0]), st_off);
   };
 
   // Cursors of tiles t + 1, t + 2, t + 3 at region t (tile t's is `cur`).

@@ -165,33 +165,51 @@ __device__ __forceinline__ void dma16(const u32x4_t& rsrc, uint32_t lds, uint32_
                : "memory", "m0");
 }
 
-// Asynchronous global -> LDS copy of rows [row0, row0 + ROWS) of a bf16 tensor whose rows
-// are `stride` elements apart, starting at column `col0` (one head), into `tile`. Rows at
-// or past `valid` read as zero (buffer range check). Every wave of the NW-wave
-// workgroup issues its share (tile_copy_insts loads); the data may be read after this
-// wave's s_waitcnt vmcnt and a barrier. Each wave instruction fills 1 KB of the tile and
-// the lane picks the global chunk that belongs at its LDS position.
-template <int D, int ROWS, int NW = 4>
-__device__ __forceinline__ void tile_copy_async(const u16* src, int64_t row0, int valid,
-                                                int64_t stride, int64_t col0, u16* tile,
-                                                int wave, int lane) {
-  constexpr int CPR = D / 8;         // chunks per row
-  constexpr int RPI = 64 / CPR;      // rows per wave instruction
-  constexpr int NI = ROWS / RPI;     // instructions per tile
-  constexpr int PER_WAVE = NI / NW;
+// Asynchronous global -> LDS copies of ROWS-row tiles of bf16 tensors whose rows are
+// `stride` elements apart (one head's D columns per row) into swizzled LDS tiles. The
+// per-lane global offsets depend only on the lane and the stride, so they are computed
+// once per kernel; a copy then costs the buffer descriptor (scalar) and its loads. Every
+// wave of the NW-wave workgroup issues its share (INSTS loads per tile); the data may be
+// read after this wave's s_waitcnt vmcnt and a barrier. Each wave instruction fills 1 KB
+// of the tile and the lane picks the global chunk that belongs at its LDS position; rows
+// at or past `valid` read as zero (buffer range check).
+template <int D, int ROWS, int NW>
+struct TileCopy {
+  static constexpr int CPR = D / 8;       // chunks per row
+  static constexpr int RPI = 64 / CPR;    // rows per wave instruction
+  static constexpr int NI = ROWS / RPI;   // instructions per tile
+  static constexpr int INSTS = NI / NW;   // per wave
   static_assert(NI % NW == 0, "tile must split over the waves");
-  const int vrows = valid < 0 ? 0 : (valid > ROWS ? ROWS : valid);
-  const uint32_t nbytes = vrows > 0 ? (uint32_t)(((int64_t)(vrows - 1) * stride + D) * 2) : 0u;
-  const u32x4_t rsrc = buffer_rsrc(src + row0 * stride + col0, nbytes);
-  const int w = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t voff[INSTS];  // this lane's byte offset from the tile's first row
+  uint32_t lds0;         // this wave's first 1 KB block, in bytes (wave-uniform)
+  int64_t stride;
+  __device__ TileCopy(int64_t stride_, int wave, int lane) : stride(stride_) {
+    const int w = __builtin_amdgcn_readfirstlane(wave);
+    lds0 = (uint32_t)(w * INSTS * 1024);
 #pragma unroll
-  for (int i = 0; i < PER_WAVE; ++i) {
-    const int ins = w * PER_WAVE + i;
-    const int r = ins * RPI + lane / CPR;
-    const int c = (lane % CPR) ^ swz<D>(r);
-    const uint32_t voff = (uint32_t)(((int64_t)r * stride + c * 8) * 2);
-    dma16(rsrc, lds_addr(tile + ins * 512), voff);
+    for (int i = 0; i < INSTS; ++i) {
+      const int r = (w * INSTS + i) * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ swz<D>(r);
+      voff[i] = (uint32_t)(((int64_t)r * stride + c * 8) * 2);
+    }
   }
+  // Rows [row0, row0 + ROWS) from column col0 of `src` into `tile`.
+  __device__ __forceinline__ void operator()(const u16* src, int64_t row0, int valid,
+                                             int64_t col0, u16* tile) const {
+    const int vrows = valid < 0 ? 0 : (valid > ROWS ? ROWS : valid);
+    const uint32_t nbytes =
+        vrows > 0 ? (uint32_t)(((int64_t)(vrows - 1) * stride + D) * 2) : 0u;
+    const u32x4_t rsrc = buffer_rsrc(src + row0 * stride + col0, nbytes);
+    const uint32_t base = lds_addr(tile) + lds0;
+#pragma unroll
+    for (int i = 0; i < INSTS; ++i) dma16(rsrc, base + i * 1024, voff[i]);
+  }
+};
+
+// Number of loads one wave issues for one TileCopy<D, ROWS, NW> copy.
+template <int D, int ROWS, int NW>
+constexpr int tile_copy_insts() {
+  return TileCopy<D, ROWS, NW>::INSTS;
 }
 
 // MFMA operand reads from a swizzled tile, with the per-lane LDS element offsets shared
@@ -264,10 +282,5 @@ __device__ __forceinline__ void wait_vmem_le() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Number of buffer_load ... lds instructions one wave issues for one tile_copy_async.
-template <int D, int ROWS, int NW>
-constexpr int tile_copy_insts() {
-  return ROWS / (64 / (D / 8)) / NW;
-}
 
 }  // namespace fcp

@@ -141,12 +141,11 @@ void fwd_kernel(FwdArgs a) {
   // one after it.
   TileCursor cur = TileCursor::first(a.segs, it.seg_begin, seg_end, it.q_off, it.q_rows);
   TileCursor nx = cur.next(a.segs, seg_end, it.q_off, it.q_rows);
+  const TileCopy<D, kFwdKt, NW> tcopy(kv_stride, wave, lane);
   auto copy = [&](const TileCursor& tc, int b) {
     const int j0n = tc.t * kFwdKt;
-    tile_copy_async<D, kFwdKt, NW>(a.k, (int64_t)tc.sg.kv_start + j0n, tc.sg.kv_len - j0n,
-                                   kv_stride, kv_col, sK[b], wave, lane);
-    tile_copy_async<D, kFwdKt, NW>(a.v, (int64_t)tc.sg.kv_start + j0n, tc.sg.kv_len - j0n,
-                                   kv_stride, kv_col, sV[b], wave, lane);
+    tcopy(a.k, (int64_t)tc.sg.kv_start + j0n, tc.sg.kv_len - j0n, kv_col, sK[b]);
+    tcopy(a.v, (int64_t)tc.sg.kv_start + j0n, tc.sg.kv_len - j0n, kv_col, sV[b]);
   };
 
   // Software pipeline over 32-key blocks. Step kb runs two regions:
