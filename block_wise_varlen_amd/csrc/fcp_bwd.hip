@@ -21,6 +21,7 @@
 // Recomputing S and dP in both kernels costs 4 of the 14 contractions per score; the
 // counted work stays the 5 of the method.
 #include "fcp_common.h"
+#include "fcp_cursor.h"
 #include "fcp_kernels.h"
 #include "fcp_types.h"
 
@@ -32,11 +33,9 @@ namespace {
 // dQ kernel
 // ---------------------------------------------------------------------------------
 
-__device__ __forceinline__ int seg_tiles(const KvSeg& s, int q_off, int rows) {
-  int last = s.kv_len - 1;
-  if (s.flags & 1) last = min(last, q_off + rows - 1 + s.mask_offset);
-  return last < 0 ? 0 : last / kKvTile + 1;
-}
+// KV tiles of the dQ kernel go through a ring of this depth (tile t + 3 is issued while
+// tile t is computed).
+constexpr int kDqRing = 4;
 
 template <int D, int CB>
 __global__ __launch_bounds__(64 * kColBlocksPerWG / CB)
@@ -45,8 +44,8 @@ void dq_kernel(BwdArgs a) {
   constexpr int NW = kColBlocksPerWG / CB;  // waves per workgroup
   constexpr int NKC = D / 16;
   constexpr int NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) u16 sK[2][kKvTile * D];
-  __shared__ __attribute__((aligned(16))) u16 sV[2][kKvTile * D];
+  __shared__ __attribute__((aligned(16))) u16 sK[kDqRing][kKvTile * D];
+  __shared__ __attribute__((aligned(16))) u16 sV[kDqRing][kKvTile * D];
 
   const int item_idx = blockIdx.x / a.n_hgroups;
   const int hg = blockIdx.x - item_idx * a.n_hgroups;
@@ -95,45 +94,36 @@ void dq_kernel(BwdArgs a) {
     for (int db = 0; db < NDB; ++db) acc[cb][db] = zero16();
 
   const int seg_end = it.seg_begin + it.seg_count;
-  int s = it.seg_begin, t = 0, nt = 0;
-  KvSeg sg{};
-  for (; s < seg_end; ++s) {
-    sg = load_uniform(a.segs, s);
-    nt = seg_tiles(sg, it.q_off, it.q_rows);
-    if (nt > 0) break;
-  }
-  bool have = s < seg_end;
   const int64_t kv_col = (int64_t)kvh * D;
   const TileCopy<D, kKvTile, NW> tcopy(kv_stride, wave, lane);
-  if (have) {
-    tcopy(a.k, sg.kv_start, sg.kv_len, kv_col, sK[0]);
-    tcopy(a.v, sg.kv_start, sg.kv_len, kv_col, sV[0]);
-    wait_vmem();
-  }
+  constexpr int NB = kDqRing;
+  constexpr int LOADS = 2 * tile_copy_insts<D, kKvTile, NW>();  // per tile, per wave
+  using Cursor = KvTileCursor<kKvTile>;
+  auto advance = [&](const Cursor& x) { return x.next(a.segs, seg_end, it.q_off, it.q_rows); };
+  auto copy = [&](const Cursor& x, int b) {
+    tcopy(a.k, (int64_t)x.sg.kv_start + x.j0(), x.sg.kv_len - x.j0(), kv_col, sK[b]);
+    tcopy(a.v, (int64_t)x.sg.kv_start + x.j0(), x.sg.kv_len - x.j0(), kv_col, sV[b]);
+  };
+  // Cursors of the tile being computed and the three after it.
+  Cursor cur = Cursor::first(a.segs, it.seg_begin, seg_end, it.q_off, it.q_rows);
+  Cursor n1 = advance(cur), n2 = advance(n1), n3 = advance(n2);
+  if (cur.valid) copy(cur, 0);
+  if (n1.valid) copy(n1, 1);
+  if (n2.valid) copy(n2, 2);
+  // Full wait: the first tiles and this lane's Q / dO registers; it also tells the
+  // compiler that none of its own loads is pending in the loop.
+  wait_vmem();
   __syncthreads();
   int buf = 0;
 
-  while (have) {
-    int ns = s, ntile = t + 1, nnt = nt;
-    KvSeg nsg = sg;
-    if (ntile >= nnt) {
-      ntile = 0;
-      for (++ns; ns < seg_end; ++ns) {
-        nsg = load_uniform(a.segs, ns);
-        nnt = seg_tiles(nsg, it.q_off, it.q_rows);
-        if (nnt > 0) break;
-      }
-    }
-    const bool next = ns < seg_end;
-    if (next) {
-      const int j0n = ntile * kKvTile;
-      tcopy(a.k, (int64_t)nsg.kv_start + j0n, nsg.kv_len - j0n, kv_col, sK[buf ^ 1]);
-      tcopy(a.v, (int64_t)nsg.kv_start + j0n, nsg.kv_len - j0n, kv_col, sV[buf ^ 1]);
-    }
-
+  while (cur.valid) {
+    // Every wave has left the slot of tile t - 1 (barrier at the end of the last
+    // iteration), so tile t + 3 may go there.
+    if (n3.valid) copy(n3, buf == 0 ? NB - 1 : buf - 1);
+    const KvSeg sg = cur.sg;
     const u16* Kt = sK[buf];
     const u16* Vt = sV[buf];
-    const int j0 = t * kKvTile;
+    const int j0 = cur.j0();
     const bool causal = sg.flags & 1;
     const bool need_mask = (j0 + kKvTile > sg.kv_len) ||
                            (causal && j0 + kKvTile - 1 - it.q_off > sg.mask_offset);
@@ -179,14 +169,20 @@ void dq_kernel(BwdArgs a) {
         }
     }
 
-    wait_vmem();
+    // Tile t + 1 must have landed (t + 2 and t + 3 may stay in flight) before the
+    // barrier that also releases this slot.
+    if (n3.valid)
+      wait_vmem_le<2 * LOADS>();
+    else if (n2.valid)
+      wait_vmem_le<LOADS>();
+    else
+      wait_vmem();
     lds_barrier();
-    buf ^= 1;
-    s = ns;
-    t = ntile;
-    nt = nnt;
-    sg = nsg;
-    have = next;
+    buf = buf == NB - 1 ? 0 : buf + 1;
+    cur = n1;
+    n1 = n2;
+    n2 = n3;
+    n3 = advance(n3);
   }
 
 #pragma unroll

@@ -24,6 +24,7 @@
 //  * K/V tiles of 64 keys go through a 3-deep LDS ring: the copy of tile n+2 is issued
 //    before the MFMAs of tile n, and tile n+1 is waited for at the end of the iteration.
 #include "fcp_common.h"
+#include "fcp_cursor.h"
 #include "fcp_kernels.h"
 #include "fcp_types.h"
 
@@ -37,44 +38,7 @@ constexpr float kRescaleSlack = 8.0f;
 // Keys per K/V tile of the forward and depth of its LDS ring.
 constexpr int kFwdKt = 128;
 
-// Number of kFwdKt-key tiles of segment `s` visible to queries [q_off, q_off + rows).
-__device__ __forceinline__ int seg_tiles(const KvSeg& s, int q_off, int rows) {
-  int last = s.kv_len - 1;
-  if (s.flags & 1) last = min(last, q_off + rows - 1 + s.mask_offset);
-  return last < 0 ? 0 : last / kFwdKt + 1;
-}
-
-// Position in the flattened (KV segment, 64-key tile) sequence of one work item, over
-// the tiles visible to queries [q_off, q_off + rows).
-struct TileCursor {
-  KvSeg sg;
-  int s, t, nt;
-  bool valid;
-  __device__ static TileCursor first(const KvSeg* segs, int s0, int s_end, int q_off,
-                                     int rows) {
-    TileCursor c{};
-    c.valid = false;
-    for (c.s = s0; c.s < s_end; ++c.s) {
-      c.sg = load_uniform(segs, c.s);
-      c.nt = seg_tiles(c.sg, q_off, rows);
-      if (c.nt > 0) {
-        c.valid = true;
-        c.t = 0;
-        break;
-      }
-    }
-    return c;
-  }
-  __device__ TileCursor next(const KvSeg* segs, int s_end, int q_off, int rows) const {
-    if (!valid) return *this;
-    if (t + 1 < nt) {
-      TileCursor c = *this;
-      c.t = t + 1;
-      return c;
-    }
-    return first(segs, s + 1, s_end, q_off, rows);
-  }
-};
+using TileCursor = KvTileCursor<kFwdKt>;
 
 // Scheduling hints (LLVM AMDGPU sched_group_barrier masks).
 constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100;
