@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false", default=True)
     ap.add_argument("--fused", action="store_true",
                     help="use the fused forward (merge folded in) inside the step")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain device copy of known size (for scaling the "
+                         "FETCH_SIZE / WRITE_SIZE counters of a profiler run)")
     return ap.parse_args()
 
 
@@ -136,10 +139,48 @@ def kernel_work(name, wl, pairs):
         parts = int(pairs["q_len"].sum())
         return parts * hq * (4 * d + 4) + q_rows * hq * (2 * d + 4), "byte", "hbm"
     if name == "bwd_delta":
-        return q_rows * hq * (4 * d + 4), "byte", "hbm"
+        # reads O, dO (bf16) and the LSE; writes (LSE in base 2, Delta)
+        return q_rows * hq * (4 * d + 12), "byte", "hbm"
     if name == "bwd_dkdv_reduce":
         return None, "byte", "hbm"   # depends on the split; never the dominant kernel
     raise KeyError(name)
+
+
+# Kernel sources whose hash a recorded HBM-traffic figure is tied to.
+KERNEL_SOURCES = ["fcp_common.h", "fcp_types.h", "fcp_kernels.h", "fcp_cursor.h",
+                  "fcp_fwd.hip", "fcp_bwd.hip", "fcp_merge.hip"]
+
+
+def sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "block_wise_varlen_amd",
+                        "csrc")
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from a committed counter summary
+    under profiles/ (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size), or
+    None when there is none or the kernel sources changed since it was taken."""
+    import glob
+    here = os.path.dirname(os.path.abspath(__file__))
+    sha = None
+    for path in sorted(glob.glob(os.path.join(here, "profiles", "*.md"))):
+        with open(path) as fh:
+            for line in fh:
+                if not line.startswith("traffic-json: "):
+                    continue
+                rec = json.loads(line[len("traffic-json: "):])
+                if rec.get("kernel") != kernel or rec.get("workload") != workload:
+                    continue
+                sha = sha or sources_sha256()
+                if rec.get("sources_sha256") == sha:
+                    return rec["bytes_per_launch"]
+    return None
 
 
 def roofline(kt, steps, wl, pairs):
@@ -152,8 +193,22 @@ def roofline(kt, steps, wl, pairs):
     else:
         achieved, peak, u = work / avg_s / 1e9, PEAK_HBM_GBS, "GB/s"
     return {"bound": bound, "kernel": name, "achieved": round(achieved, 2), "peak": peak,
-            "unit": u, "frac": round(achieved / peak, 4), "traffic": None,
+            "unit": u, "frac": round(achieved / peak, 4),
+            "traffic": recorded_traffic(name, wl.name),
             "avg_launch_ms": round(total_ms / launches, 4), "launches": launches}
+
+
+def calibration_copy(n_bytes=512 << 20, reps=3):
+    """A plain device-to-device copy of n_bytes (read n_bytes, write n_bytes per launch),
+    whose FETCH_SIZE / WRITE_SIZE counters scale the other kernels' counts to bytes."""
+    import torch
+    src = torch.empty(n_bytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("calibration copy: %d bytes read and %d bytes written per launch, %d launches"
+        % (n_bytes, n_bytes, reps))
 
 
 def cpu_baseline(wl, seed):
@@ -242,6 +297,8 @@ def main():
         del bits
     else:
         dev = W.make_device_inputs(wl, seed=args.seed)
+    if args.calibrate_copy:
+        calibration_copy()
     path = Path(wl, dev, fused=args.fused)
     pairs = build_pairs(wl)
     fl_f, fl_b = W.fwd_flops(wl), W.bwd_flops(wl)
