@@ -67,3 +67,29 @@ def sample_rows(wl, n, seed=0):
         rows.update({s.row0, s.row0 + s.length - 1, s.row0 + s.length // 2})
     rows.update(rng.integers(0, wl.q_rows, size=n).tolist())
     return np.array(sorted(rows), dtype=np.int64)
+
+
+class DeviceRows:
+    """Float64 view of a device bf16 tensor [rows, heads, D] for the oracle at full size:
+    ``x[row_array, head]`` copies just those rows of one head to the host (exactly: bf16
+    -> float64). The last fetch is cached, since the oracle reads the same key rows for
+    every query head of a KV group."""
+
+    def __init__(self, t):
+        self.t = t
+        self._key = None
+        self._val = None
+
+    def __getitem__(self, key):
+        import torch
+        rows, h = key
+        rows = np.asarray(rows, dtype=np.int64)
+        ck = (id(rows) if rows.base is None else id(rows.base), rows.shape,
+              int(rows[0]) if rows.size else -1, int(rows[-1]) if rows.size else -1, int(h))
+        if ck == self._key:
+            return self._val
+        idx = torch.as_tensor(rows, device=self.t.device)
+        val = bf16_to_f64(self.t[:, h].index_select(0, idx))
+        if rows.size > 4096:
+            self._key, self._val = ck, val
+        return val

@@ -116,3 +116,43 @@ def test_full_size_sampled(gpu, cfg):
         rhs = do_h[qr].reshape(len(qr), wl.num_kv_heads, g, -1).sum(axis=(0, 2))
         rel = np.linalg.norm(lhs - rhs) / np.linalg.norm(rhs)
         assert rel < 2e-2, (s, rel)
+
+
+def test_full_size_heterogeneous(gpu):
+    """The heaviest worker of the heterogeneous batch (33 Q blocks of many packed
+    sequences, up to 511K tokens long), forward + backward as the bench runs it: dQ on
+    sampled rows against the oracle, and per sequence and KV head the sum of dV over all
+    keys against the sum of dO over the owned queries (rows of P sum to one)."""
+    import torch
+    wl = W.config5(0)
+    dev = W.make_device_inputs(wl, seed=0)
+    pairs = build_pairs(wl)
+    _, _, dq, dk, dv = _fwd_bwd(wl, dev, pairs)
+    torch.cuda.synchronize()
+    assert not torch.isnan(dk).any() and not torch.isnan(dv).any()
+    idx = oracle.SeqIndex(wl)
+    rng = np.random.default_rng(11)
+    rows = U.sample_rows(wl, 8, seed=11)
+    if len(rows) > 24:
+        rows = np.sort(rng.choice(rows, 24, replace=False))
+    rq = oracle.dq_rows(U.DeviceRows(dev["q"]), U.DeviceRows(dev["k"]), U.DeviceRows(dev["v"]),
+                        U.DeviceRows(dev["do"]), idx, rows)
+    check_grad(dq.index_select(0, torch.as_tensor(rows, device=dq.device)).cpu().numpy(), rq,
+               "config5 dQ rows")
+    g = wl.num_q_heads // wl.num_kv_heads
+    owned = set(np.unique(idx.q_row_seq[idx.owned_rows()]).tolist())
+    for s in sorted(owned):
+        # Keys past the last owned query of the sequence are not in the KV buffer (-1);
+        # no owned query sees them.
+        kpos = np.asarray(idx.kv_row_of_pos[s])
+        kpos = kpos[kpos >= 0]
+        assert kpos.size and kpos.max() < wl.kv_rows
+        qpos = np.nonzero(idx.q_row_seq == s)[0]
+        assert qpos.size and qpos.max() < wl.q_rows
+        kr = torch.as_tensor(kpos, device=dv.device)
+        qr = torch.as_tensor(qpos, device=dv.device)
+        lhs = dv.index_select(0, kr).double().sum(dim=0)
+        rhs = dev["do"].index_select(0, qr).double().reshape(len(qr), wl.num_kv_heads, g, -1) \
+            .sum(dim=(0, 2))
+        rel = (torch.linalg.norm(lhs - rhs) / torch.linalg.norm(rhs)).item()
+        assert rel < 2e-2, (s, rel)

@@ -117,6 +117,32 @@ def test_full_size_sampled(gpu, cfg):
                  lf.index_select(0, ridx).cpu().numpy(), o_ref, l_ref, cfg + " fused")
 
 
+@pytest.mark.parametrize("cfg", ["config4", "config5"])
+def test_full_size_zigzag_and_heterogeneous(gpu, cfg):
+    """The Zig-Zag worker (512K sequence, Q blocks 0 and 127, 33 coalesced KV ranges) and
+    the heaviest worker of the heterogeneous batch, per-pair partials + merge as the bench
+    runs them, on sampled rows (inputs drawn on the device; the oracle reads the rows it
+    needs from there)."""
+    import torch
+    wl = W.config4(0) if cfg == "config4" else W.config5(0)
+    dev = W.make_device_inputs(wl, seed=0, which=("q", "k", "v"))
+    pairs = build_pairs(wl)
+    o_part, lse_part = _run_partials(wl, dev, pairs)
+    o, lse = B.fcp_merge_partials(pairs, o_part, lse_part, wl.q_rows, wl.num_kv_heads)
+    del o_part, lse_part
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    rows = U.sample_rows(wl, 12, seed=7)
+    if len(rows) > 40:   # many packed segments: keep boundaries of a random subset
+        rows = np.sort(rng.choice(rows, 40, replace=False))
+    idx = oracle.SeqIndex(wl)
+    o_ref, l_ref = oracle.forward(U.DeviceRows(dev["q"]), U.DeviceRows(dev["k"]),
+                                  U.DeviceRows(dev["v"]), idx, rows=rows)
+    ridx = torch.as_tensor(rows, device=o.device)
+    U.check_attn(U.bf16_to_f64(o.index_select(0, ridx)), lse.index_select(0, ridx).cpu().numpy(),
+                 o_ref, l_ref, cfg + " merge")
+
+
 def test_error_paths_do_not_launch(gpu):
     import torch
     wl = W.config1()
