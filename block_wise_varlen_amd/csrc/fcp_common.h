@@ -48,43 +48,6 @@ __device__ __forceinline__ void agpr_settle(f32x16_t& acc) {
   asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+a"(acc));
 }
 
-// acc (VGPRs) = a * b (early-clobber, no C input) and acc += a * b, issued through
-// inline assembly so that they keep their place in the instruction stream (the compiler
-// keeps volatile asm in program order): kernels interleave them with the VALU work of
-// another block by writing the two in alternation. The leading wait states cover a VALU
-// write of a or b just before; VALU reads of acc must follow vsettle().
-__device__ __forceinline__ void mfma32_v_first(f32x16_t& acc, bf16x8_t a, bf16x8_t b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma32_v(f32x16_t& acc, bf16x8_t a, bf16x8_t b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
-}
-// Wait states after the last MFMA writing these registers before VALU reads them (a
-// 16-pass MFMA result needs 18; 40 are given).
-__device__ __forceinline__ void vsettle(f32x16_t& x) {
-  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+v"(x));
-}
-template <int N>
-__device__ __forceinline__ void vsettle_all(f32x16_t (&x)[N]) {
-  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" ::: "memory");
-#pragma unroll
-  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(x[i]));
-}
-
-// acc (VGPRs) = a * b, and acc += a * b, with the B operand read from accumulation
-// registers: a stationary operand parked there leaves the VGPRs to streamed operands.
-// As these are opaque to the compiler's hazard tracking, VALU reads of acc must follow
-// vgpr_settle().
-__device__ __forceinline__ void mfma32_ab_first(f32x16_t& acc, bf16x8_t a, const bf16x8_t& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "a"(b));
-}
-__device__ __forceinline__ void mfma32_ab(f32x16_t& acc, bf16x8_t a, const bf16x8_t& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
-}
-__device__ __forceinline__ void vgpr_settle(f32x16_t& x, f32x16_t& y) {
-  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+v"(x), "+v"(y));
-}
-
 __device__ __forceinline__ f32x16_t zero16() {
   f32x16_t z;
 #pragma unroll
