@@ -47,7 +47,31 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of known size (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters of a profiler run)")
+    ap.add_argument("--comm-plan", action="store_true",
+                    help="instead of the attention step, time the host-only congestion-free "
+                         "planner on Zig-Zag pull graphs of 64..512 workers and on the "
+                         "heterogeneous 64-worker batch (one JSON line per graph; no GPU)")
     return ap.parse_args()
+
+
+def comm_plan_bench(repeats=5):
+    """Wall time of fcp_comm_plan (median of ``repeats``) on FCP pull graphs."""
+    import fcp_workloads as W
+    from block_wise_varlen_amd import binding as B
+    B.load()
+    graphs = [("zigzag-N%d-b4096" % n, n, W.zigzag_graph(n, seqlen=2 * n * 4096))
+              for n in (64, 128, 256, 512)]
+    graphs.append(("hetero-lognormal8K-128Kx64-b4096-lpt", 64, W.hetero_graph()))
+    for name, n, (src, dst) in graphs:
+        times = []
+        for _ in range(repeats):
+            t0 = time.perf_counter()
+            _, k = B.fcp_comm_plan(n, src, dst)
+            times.append((time.perf_counter() - t0) * 1e3)
+        print(json.dumps({"metric": "comm_plan_ms", "value": round(sorted(times)[len(times) // 2], 3),
+                          "unit": "ms", "higher_is_better": False,
+                          "config": {"graph": name, "workers": n, "transfers": int(len(src)),
+                                     "stages": k}}), flush=True)
 
 
 class Path:
@@ -276,6 +300,9 @@ def main():
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
+    if args.comm_plan:
+        comm_plan_bench()
+        return
     import torch
     import fcp_workloads as W
     from fcp_workloads.tensors import host_to_device

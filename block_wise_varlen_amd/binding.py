@@ -23,7 +23,7 @@ FCP_OP_FWD, FCP_OP_MERGE, FCP_OP_BWD, FCP_OP_FWD_FUSED = range(4)
 SYMBOLS = ("fcp_abi_version", "fcp_status_string", "fcp_last_error", "fcp_validate",
            "fcp_workspace_bytes", "fcp_block_attn_fwd", "fcp_merge_partials",
            "fcp_block_attn_fwd_fused", "fcp_block_attn_bwd", "fcp_timing_enable",
-           "fcp_timing_read", "fcp_kernel_name")
+           "fcp_timing_read", "fcp_kernel_name", "fcp_comm_plan")
 FCP_KERNEL_COUNT = 7
 
 
@@ -75,6 +75,7 @@ def load():
         "fcp_timing_enable": (ctypes.c_int, [ctypes.c_int]),
         "fcp_timing_read": (ctypes.c_int, [P, P, I32]),
         "fcp_kernel_name": (ctypes.c_char_p, [ctypes.c_int]),
+        "fcp_comm_plan": (ctypes.c_int, [I32, I32, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -283,3 +284,20 @@ def fcp_timing_read():
     _check(load().fcp_timing_read(ctypes.cast(tot, ctypes.c_void_p),
                                   ctypes.cast(cnt, ctypes.c_void_p), FCP_KERNEL_COUNT))
     return {fcp_kernel_name(i): (tot[i], cnt[i]) for i in range(FCP_KERNEL_COUNT) if cnt[i]}
+
+
+# ---- congestion-free communication plan (host only) --------------------------------
+
+def fcp_comm_plan(n_workers, src, dst):
+    """(stage per edge as int32 ndarray, number of stages) for the transfers src[e] -> dst[e]."""
+    src = np.ascontiguousarray(src, dtype=np.int32)
+    dst = np.ascontiguousarray(dst, dtype=np.int32)
+    if src.shape != dst.shape or src.ndim != 1:
+        raise ValueError("src and dst must be 1-D arrays of equal length")
+    stage = np.empty_like(src)
+    n = ctypes.c_int32(0)
+    _check(load().fcp_comm_plan(int(n_workers), int(src.size), src.ctypes.data_as(ctypes.c_void_p),
+                                dst.ctypes.data_as(ctypes.c_void_p),
+                                stage.ctypes.data_as(ctypes.c_void_p),
+                                ctypes.cast(ctypes.byref(n), ctypes.c_void_p)))
+    return stage, n.value

@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "fcp.h"
+#include "fcp_comm.h"
 #include "fcp_kernels.h"
 #include "fcp_plan.h"
 
@@ -400,6 +401,15 @@ int fcp_block_attn_bwd(const fcp_dims_t* dims, const void* q, const void* k, con
       if (e != hipSuccess) return hip_err(e, "dK/dV reduce launch");
     }
     return FCP_OK;
+  });
+}
+
+int fcp_comm_plan(int32_t n_workers, int32_t n_edges, const int32_t* src, const int32_t* dst,
+                  int32_t* stage, int32_t* n_stages) {
+  return guarded([&] {
+    std::string msg;
+    const int st = fcp::comm_plan(n_workers, n_edges, src, dst, stage, n_stages, &msg);
+    return st == FCP_OK ? st : set_err(st, msg);
   });
 }
 

@@ -84,16 +84,58 @@ def config5(seed=0, n_workers=64, budget_per_worker=131072, block=4096, coalesce
     if worker is None:
         worker = max(range(n_workers), key=lambda w: (load[w], -w))
     q_ids = [i for i, w in enumerate(assign) if w == worker]
-    need = {}
-    for i in q_ids:
-        for s in blocks[i]:
-            need[s.seq] = max(need.get(s.seq, 0), s.pos0 + s.length)
-    kv_ids = [i for i, blk in enumerate(blocks)
-              if any(s.seq in need and s.pos0 < need[s.seq] for s in blk)]
+    kv_ids = kv_needs(blocks, q_ids)
     return _wl(CONFIG_NAMES[5], seqlens, block, 64, 8, 128, True, q_ids, kv_ids, blocks,
                coalesce=coalesce, rng="device",
                meta={"seed": seed, "worker": worker, "load": load, "tokens": tokens,
                      "assign": assign, "n_blocks": len(blocks)})
+
+
+def kv_needs(blocks, q_ids):
+    """Ids of the blocks whose keys the Q blocks ``q_ids`` attend to causally: every block
+    holding a position of one of their sequences below the last query position."""
+    need = {}
+    for i in q_ids:
+        for s in blocks[i]:
+            need[s.seq] = max(need.get(s.seq, 0), s.pos0 + s.length)
+    return [i for i, blk in enumerate(blocks)
+            if any(s.seq in need and s.pos0 < need[s.seq] for s in blk)]
+
+
+def pull_graph(blocks, assign, n_workers):
+    """The block transfers of one causal forward (FCP paper Sec. 4.2, Figure 8): every
+    block's K/V live with the worker its Q is assigned to, and every worker pulls each
+    block it needs that another worker holds. Returns (src, dst) int32 arrays, one entry
+    per transfer, sorted by receiver then block id."""
+    src, dst = [], []
+    for w in range(n_workers):
+        mine = [i for i, a in enumerate(assign) if a == w]
+        for j in kv_needs(blocks, mine):
+            if assign[j] != w:
+                src.append(assign[j])
+                dst.append(w)
+    return np.asarray(src, dtype=np.int32), np.asarray(dst, dtype=np.int32)
+
+
+def zigzag_graph(n_workers=64, seqlen=524288, block=4096):
+    """Pull graph of the Zig-Zag assignment of one sequence: worker w holds blocks w and
+    2N-1-w (FCP paper Sec. 3.2, Figure 4)."""
+    blocks = pack_stream([seqlen], block)
+    n = len(blocks)
+    assert n == 2 * n_workers
+    assign = [b if b < n_workers else n - 1 - b for b in range(n)]
+    return pull_graph(blocks, assign, n_workers)
+
+
+def hetero_graph(seed=0, n_workers=64, budget_per_worker=131072, block=4096):
+    """Pull graph of the heterogeneous lognormal batch with its LPT assignment (the
+    workload of ``config5``, all workers)."""
+    rng = np.random.default_rng(seed)
+    seqlens = lognormal_lengths(rng, 8192, 1.5, 1, 524288, n_workers * budget_per_worker)
+    blocks = shard_ffd(seqlens, block)
+    costs = [block_cost(b) for b in blocks]
+    assign, _, _ = lpt_assign(blocks, costs, n_workers, budget_per_worker + block)
+    return pull_graph(blocks, assign, n_workers)
 
 
 def custom(seqlens, block, hq, hkv, d, causal=True, q_ids=None, kv_ids=None,

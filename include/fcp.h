@@ -217,6 +217,22 @@ int fcp_timing_enable(int on);
 int fcp_timing_read(double* total_ms, int32_t* launches, int32_t n);
 const char* fcp_kernel_name(int id);
 
+/*
+ * Congestion-free communication plan (FCP paper Sec. 4.2, "Congestion-free solver",
+ * Lemmas 1 and 2). Host only: no GPU, no stream, callable anywhere. The n_edges block
+ * transfers among n_workers workers form a bipartite multigraph (edge e: worker src[e]
+ * sends one block to worker dst[e]; src[e] == dst[e] is allowed and counts once on each
+ * side). Writes stage[e] for every edge so that within one stage no worker sends more
+ * than one block and none receives more than one (each stage is a matching), using the
+ * minimum possible number of stages, the maximal send-or-receive degree Delta, returned
+ * in *n_stages. Stages are numbered 0..Delta-1 and each is non-empty. Host arrays of
+ * n_edges int32 each, owned by the caller; n_edges == 0 gives *n_stages = 0. A worker id
+ * outside [0, n_workers) or a NULL array is FCP_ERR_INVALID_ARG. Coalescing c sub-stages
+ * into one (the pages' knob for launch overhead) is stage[e] / c.
+ */
+int fcp_comm_plan(int32_t n_workers, int32_t n_edges, const int32_t* src, const int32_t* dst,
+                  int32_t* stage, int32_t* n_stages);
+
 #ifdef __cplusplus
 }
 #endif
