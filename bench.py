@@ -47,11 +47,92 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of known size (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters of a profiler run)")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="instead of the attention step, time the block-level pipelined "
+                         "forward of the Zig-Zag worker (pulls overlapped with compute) "
+                         "against the same stages with every block already resident")
     ap.add_argument("--comm-plan", action="store_true",
                     help="instead of the attention step, time the host-only congestion-free "
                          "planner on Zig-Zag pull graphs of 64..512 workers and on the "
                          "heterogeneous 64-worker batch (one JSON line per graph; no GPU)")
     return ap.parse_args()
+
+
+def pipeline_bench(args):
+    """eta of FCP paper Sec. 3.3 on one GPU: time of the pipelined forward of Zig-Zag
+    worker 0 of 64 (126 blocks pulled in the congestion-free order, 4 per stage, copies
+    on a second stream) over the time of the same stages with every block resident."""
+    import numpy as np
+    import torch
+    import fcp_workloads as W
+    from block_wise_varlen_amd import binding as B
+    from block_wise_varlen_amd.descriptors import build_pipeline
+    wl = W.config4(0)
+    src, dst, blk = W.zigzag_graph(64)
+    stage, _ = B.fcp_comm_plan(64, src, dst)
+    m = dst == 0
+    recv = {int(b): int(s) for b, s in zip(blk[m], stage[m])}
+    dev = W.make_device_inputs(wl, seed=args.seed, which=("q", "k", "v"))
+    hkv, d, hq = wl.num_kv_heads, wl.head_dim, wl.num_q_heads
+
+    def buffers(P, fill):
+        k = torch.zeros((P["kv_rows"], hkv, d), dtype=torch.bfloat16, device="cuda")
+        v = torch.zeros_like(k)
+        for c in fill:
+            s0, t0, n = int(c["src_row"]), int(c["dst_row"]), int(c["n_rows"])
+            k[t0:t0 + n] = dev["k"][s0:s0 + n]
+            v[t0:t0 + n] = dev["v"][s0:s0 + n]
+        return k, v
+
+    pipe = build_pipeline(wl, wl.q_block_ids, recv, coalesce=4)
+    res = build_pipeline(wl, wl.q_block_ids, recv, coalesce=4, slots=None)
+    # Resident: every stage's blocks already in place, no copies in the tables.
+    res_fill = np.concatenate([res["local_copies"], res["copies"]])
+    res_stages = res["stages"].copy()
+    res_stages["n_copies"] = 0
+    kp, vp = buffers(pipe, pipe["local_copies"])
+    kr, vr = buffers(res, res_fill)
+    o_part = torch.empty((pipe["part_rows"], hq, d), dtype=torch.float32, device="cuda")
+    lse_part = torch.empty((pipe["part_rows"], hq), dtype=torch.float32, device="cuda")
+    o = torch.empty_like(dev["q"])
+    lse = torch.empty((wl.q_rows, hq), dtype=torch.float32, device="cuda")
+    cs = torch.cuda.Stream()
+    nothing = np.zeros(0, dtype=pipe["copies"].dtype)
+    legs = {
+        "resident": lambda: B.fcp_pipeline_fwd(dev["q"], kr, vr, dev["k"], dev["v"], res_stages,
+                                               nothing, res["pairs"], o_part, lse_part, o, lse),
+        "overlap_dma": lambda: B.fcp_pipeline_fwd(dev["q"], kp, vp, dev["k"], dev["v"],
+                                                  pipe["stages"], pipe["copies"], pipe["pairs"],
+                                                  o_part, lse_part, o, lse, copy_stream=cs),
+        "overlap_shader": lambda: B.fcp_pipeline_fwd(
+            dev["q"], kp, vp, dev["k"], dev["v"], pipe["stages"], pipe["copies"], pipe["pairs"],
+            o_part, lse_part, o, lse, flags=B.FCP_PIPE_COPY_SHADER, copy_stream=cs),
+        "serial_dma": lambda: B.fcp_pipeline_fwd(dev["q"], kp, vp, dev["k"], dev["v"],
+                                                 pipe["stages"], pipe["copies"], pipe["pairs"],
+                                                 o_part, lse_part, o, lse),
+    }
+    ms, copy_rate = {}, {}
+    copy_bytes = 2 * int(pipe["copies"]["n_rows"].sum()) * hkv * d * 2
+    for name, fn in legs.items():
+        log("timing pipeline leg", name)
+        ms[name], kt = timed(fn, args.steps, args.warmup, True)
+        if "pipe_copy" in kt:
+            t, n = kt["pipe_copy"]
+            copy_rate[name] = round(copy_bytes * n / args.steps / (t * 1e-3) / 1e9, 1)
+    flops = W.fwd_flops(wl)
+    result = {
+        "metric": "pipeline_eta", "value": round(ms["overlap_dma"] / ms["resident"], 4),
+        "unit": "ratio", "higher_is_better": False, "steps": args.steps, "warmup": args.warmup,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name + "-pipelined", "worker": 0, "n_workers": 64,
+                   "stages": len(pipe["stages"]), "pulled_blocks": len(recv),
+                   "copy_bytes_per_step": copy_bytes},
+        "ms_per_step": {k: round(v, 3) for k, v in ms.items()},
+        "eta": {k: round(v / ms["resident"], 4) for k, v in ms.items()},
+        "fwd_tflops": {k: round(flops / v / 1e9, 1) for k, v in ms.items()},
+        "copy_GBps": copy_rate,
+    }
+    print(json.dumps(result), flush=True)
 
 
 def comm_plan_bench(repeats=5):
@@ -62,7 +143,7 @@ def comm_plan_bench(repeats=5):
     graphs = [("zigzag-N%d-b4096" % n, n, W.zigzag_graph(n, seqlen=2 * n * 4096))
               for n in (64, 128, 256, 512)]
     graphs.append(("hetero-lognormal8K-128Kx64-b4096-lpt", 64, W.hetero_graph()))
-    for name, n, (src, dst) in graphs:
+    for name, n, (src, dst, _) in graphs:
         times = []
         for _ in range(repeats):
             t0 = time.perf_counter()
@@ -302,6 +383,13 @@ def main():
         sys.exit(2)
     if args.comm_plan:
         comm_plan_bench()
+        return
+    if args.pipeline:
+        import torch
+        if not torch.cuda.is_available():
+            print("no GPU available", file=sys.stderr)
+            sys.exit(1)
+        pipeline_bench(args)
         return
     import torch
     import fcp_workloads as W

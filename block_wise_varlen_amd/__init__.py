@@ -8,5 +8,6 @@ host; ``binding`` exposes the C entry points under their own names.
 from .descriptors import build_pairs, part_rows, PAIR_DTYPE, FLAG_CAUSAL
 from .binding import (fcp_abi_version, fcp_status_string, fcp_last_error, fcp_validate,
                       fcp_workspace_bytes, fcp_block_attn_fwd, fcp_merge_partials,
-                      fcp_block_attn_fwd_fused, fcp_block_attn_bwd, fcp_comm_plan, make_dims,
-                      FcpError, FCP_OP_FWD, FCP_OP_MERGE, FCP_OP_BWD, FCP_OP_FWD_FUSED)
+                      fcp_block_attn_fwd_fused, fcp_block_attn_bwd, fcp_comm_plan,
+                      fcp_pipeline_fwd, fcp_pipeline_workspace_bytes, make_dims, FcpError,
+                      FCP_OP_FWD, FCP_OP_MERGE, FCP_OP_BWD, FCP_OP_FWD_FUSED)

@@ -11,7 +11,7 @@ import os
 
 import numpy as np
 
-from .descriptors import PAIR_DTYPE, PAIR_FIELDS
+from .descriptors import PAIR_DTYPE, PAIR_FIELDS, COPY_DTYPE, STAGE_DTYPE
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfcp.so")
 
@@ -23,8 +23,10 @@ FCP_OP_FWD, FCP_OP_MERGE, FCP_OP_BWD, FCP_OP_FWD_FUSED = range(4)
 SYMBOLS = ("fcp_abi_version", "fcp_status_string", "fcp_last_error", "fcp_validate",
            "fcp_workspace_bytes", "fcp_block_attn_fwd", "fcp_merge_partials",
            "fcp_block_attn_fwd_fused", "fcp_block_attn_bwd", "fcp_timing_enable",
-           "fcp_timing_read", "fcp_kernel_name", "fcp_comm_plan")
-FCP_KERNEL_COUNT = 7
+           "fcp_timing_read", "fcp_kernel_name", "fcp_comm_plan", "fcp_pipeline_fwd",
+           "fcp_pipeline_workspace_bytes")
+FCP_KERNEL_COUNT = 8
+FCP_PIPE_COPY_SHADER = 1
 
 
 class FcpError(RuntimeError):
@@ -76,6 +78,9 @@ def load():
         "fcp_timing_read": (ctypes.c_int, [P, P, I32]),
         "fcp_kernel_name": (ctypes.c_char_p, [ctypes.c_int]),
         "fcp_comm_plan": (ctypes.c_int, [I32, I32, P, P, P, P]),
+        "fcp_pipeline_fwd": (ctypes.c_int, [D, P, P, P, P, P, ctypes.c_int64, P, I32, P, P,
+                                            P, P, P, P, I32, P, SZ, P, P]),
+        "fcp_pipeline_workspace_bytes": (SZ, [D, P, I32, P, P, ctypes.c_int64]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -265,6 +270,55 @@ def fcp_block_attn_bwd(q, k, v, o, lse, dout, pairs, dq=None, dk=None, dv=None,
                                   _ptr(lse), _ptr(dout), p, n, _ptr(dq), _ptr(dk), _ptr(dv),
                                   _ptr(ws), wsb, _stream(q, stream)))
     return dq, dk, dv
+
+
+def _table(x, dtype):
+    arr = np.ascontiguousarray(np.asarray(x, dtype=dtype))
+    return arr, arr.ctypes.data_as(ctypes.c_void_p), len(arr)
+
+
+def fcp_pipeline_workspace_bytes(dims, stages, copies, pairs, src_rows):
+    st, sp, ns = _table(stages, STAGE_DTYPE)
+    cp, cpp, _ = _table(copies, COPY_DTYPE)
+    pr, pp, _ = _table(pairs, PAIR_DTYPE)
+    return load().fcp_pipeline_workspace_bytes(ctypes.byref(dims), sp, ns, cpp, pp,
+                                               int(src_rows))
+
+
+def fcp_pipeline_fwd(q, k, v, k_src, v_src, stages, copies, pairs, o_part, lse_part, o=None,
+                     lse=None, flags=0, softmax_scale=0.0, ws=None, stream=None,
+                     copy_stream=None):
+    """Pipelined forward: per stage, copies from k_src/v_src into k/v on ``copy_stream``
+    overlapping the previous stage's pairs on ``stream``; then the merge into o/lse.
+    ``copy_stream=None`` uses ``stream`` (no overlap). k and v are written."""
+    import torch
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (k_src, "k_src"), (v_src, "v_src")):
+        _need(t, torch.bfloat16, nm)
+    _need(o_part, torch.float32, "o_part")
+    _need(lse_part, torch.float32, "lse_part")
+    if o is None:
+        o = torch.zeros_like(q)
+    if lse is None:
+        lse = torch.zeros((q.shape[0], q.shape[1]), dtype=torch.float32, device=q.device)
+    _need(o, torch.bfloat16, "o")
+    _need(lse, torch.float32, "lse")
+    if k_src.shape[1:] != k.shape[1:] or v_src.shape != k_src.shape or v.shape != k.shape:
+        raise ValueError("k/v and k_src/v_src must have matching row layouts")
+    st, sp, ns = _table(stages, STAGE_DTYPE)
+    cp, cpp, _ = _table(copies, COPY_DTYPE)
+    pr, pp, _ = _table(pairs, PAIR_DTYPE)
+    dims = _dims_from(q, k, o_part.shape[0], softmax_scale)
+    lib = load()
+    src_rows = k_src.shape[0]
+    ws, wsb = _workspace(lambda: lib.fcp_pipeline_workspace_bytes(ctypes.byref(dims), sp, ns,
+                                                                  cpp, pp, src_rows), q, ws)
+    s = _stream(q, stream)
+    cs = s if copy_stream is None else ctypes.c_void_p(copy_stream.cuda_stream)
+    _check(lib.fcp_pipeline_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(k_src),
+                                _ptr(v_src), src_rows, sp, ns, cpp, pp, _ptr(o_part),
+                                _ptr(lse_part), _ptr(o), _ptr(lse), int(flags), _ptr(ws), wsb,
+                                s, cs))
+    return o, lse
 
 
 # ---- per-kernel timing ------------------------------------------------------------

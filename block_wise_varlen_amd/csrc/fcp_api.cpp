@@ -14,6 +14,7 @@
 #include "fcp.h"
 #include "fcp_comm.h"
 #include "fcp_kernels.h"
+#include "fcp_pipeline.h"
 #include "fcp_plan.h"
 
 namespace {
@@ -40,8 +41,8 @@ struct Staging {
 std::mutex g_pool_mu;
 std::vector<std::unique_ptr<Staging>> g_pool;
 
-int upload(const fcp::Plan& P, void* ws, hipStream_t stream) {
-  const size_t n = P.blob.size();
+int upload(const std::vector<uint8_t>& blob, void* ws, hipStream_t stream) {
+  const size_t n = blob.size();
   if (n == 0) return FCP_OK;
   Staging* st = nullptr;
   {
@@ -64,7 +65,7 @@ int upload(const fcp::Plan& P, void* ws, hipStream_t stream) {
     }
     st->busy = true;
   }
-  std::memcpy(st->ptr, P.blob.data(), n);
+  std::memcpy(st->ptr, blob.data(), n);
   hipError_t e = hipMemcpyAsync(ws, st->ptr, n, hipMemcpyHostToDevice, stream);
   if (e == hipSuccess) e = hipEventRecord(st->ev, stream);
   {
@@ -73,6 +74,41 @@ int upload(const fcp::Plan& P, void* ws, hipStream_t stream) {
   }
   if (e != hipSuccess) return hip_err(e, "work-list upload");
   return FCP_OK;
+}
+
+// Events that order the pipeline's two streams. An event goes back to the pool once the
+// work it marks has completed, so a later call never re-records one that a pending wait
+// may still refer to.
+std::mutex g_ev_mu;
+std::vector<hipEvent_t> g_ev_pool;
+
+int take_sync_events(size_t n, std::vector<hipEvent_t>* out) {
+  std::lock_guard<std::mutex> lk(g_ev_mu);
+  for (size_t i = 0; i < g_ev_pool.size() && out->size() < n;) {
+    if (hipEventQuery(g_ev_pool[i]) == hipSuccess) {
+      out->push_back(g_ev_pool[i]);
+      g_ev_pool[i] = g_ev_pool.back();
+      g_ev_pool.pop_back();
+    } else {
+      ++i;
+    }
+  }
+  while (out->size() < n) {
+    hipEvent_t e = nullptr;
+    const hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+    if (r != hipSuccess) {
+      g_ev_pool.insert(g_ev_pool.end(), out->begin(), out->end());
+      out->clear();
+      return hip_err(r, "hipEventCreate(pipeline)");
+    }
+    out->push_back(e);
+  }
+  return FCP_OK;
+}
+
+void give_back_events(const std::vector<hipEvent_t>& evs) {
+  std::lock_guard<std::mutex> lk(g_ev_mu);
+  g_ev_pool.insert(g_ev_pool.end(), evs.begin(), evs.end());
 }
 
 // The kernels are written for gfx950 only.
@@ -162,7 +198,7 @@ int prepare(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t n, int op,
                                           std::to_string(P->ws_bytes) + " bytes");
   st = check_device();
   if (st != FCP_OK) return st;
-  return upload(*P, ws, stream);
+  return upload(P->blob, ws, stream);
 }
 
 template <class T>
@@ -243,7 +279,7 @@ int fcp_timing_read(double* total_ms, int32_t* launches, int32_t n) {
 const char* fcp_kernel_name(int id) {
   static const char* names[FCP_KERNEL_COUNT] = {"fwd_partial", "fwd_fused", "merge",
                                                 "bwd_delta",   "bwd_dq",    "bwd_dkdv",
-                                                "bwd_dkdv_reduce"};
+                                                "bwd_dkdv_reduce", "pipe_copy"};
   return (id >= 0 && id < FCP_KERNEL_COUNT) ? names[id] : "";
 }
 
@@ -401,6 +437,130 @@ int fcp_block_attn_bwd(const fcp_dims_t* dims, const void* q, const void* k, con
       if (e != hipSuccess) return hip_err(e, "dK/dV reduce launch");
     }
     return FCP_OK;
+  });
+}
+
+size_t fcp_pipeline_workspace_bytes(const fcp_dims_t* dims, const fcp_stage_t* stages,
+                                    int32_t n_stages, const fcp_copy_t* copies,
+                                    const fcp_pair_t* pairs, int64_t src_rows) {
+  size_t out = 0;
+  guarded([&] {
+    fcp::PipelinePlan P;
+    std::string msg;
+    const int st =
+        fcp::make_pipeline_plan(dims, stages, n_stages, copies, pairs, src_rows, &P, &msg);
+    if (st != FCP_OK) return set_err(st, msg);
+    out = P.ws_bytes;
+    return FCP_OK;
+  });
+  return out;
+}
+
+int fcp_pipeline_fwd(const fcp_dims_t* dims, const void* q, void* k, void* v,
+                     const void* k_src, const void* v_src, int64_t src_rows,
+                     const fcp_stage_t* stages, int32_t n_stages, const fcp_copy_t* copies,
+                     const fcp_pair_t* pairs, float* o_part, float* lse_part, void* o,
+                     float* lse, int32_t flags, void* ws, size_t ws_bytes,
+                     hipStream_t stream, hipStream_t copy_stream) {
+  return guarded([&] {
+    if (flags & ~FCP_PIPE_COPY_SHADER) return set_err(FCP_ERR_INVALID_ARG, "unknown flag bits");
+    fcp::PipelinePlan P;
+    std::string msg;
+    int st = fcp::make_pipeline_plan(dims, stages, n_stages, copies, pairs, src_rows, &P, &msg);
+    if (st != FCP_OK) return set_err(st, msg);
+    if (P.n_pairs == 0 && P.n_copies == 0) return FCP_OK;
+    st = need_ptrs({k, v});
+    if (st == FCP_OK && P.n_copies > 0) st = need_ptrs({k_src, v_src});
+    if (st == FCP_OK && P.n_pairs > 0) st = need_ptrs({q, o_part, lse_part, o, lse});
+    if (st != FCP_OK) return st;
+    if (P.n_pairs > 0 && (!ws || ws_bytes < P.ws_bytes || !aligned16(ws)))
+      return set_err(FCP_ERR_WORKSPACE, "workspace missing, misaligned or smaller than " +
+                                            std::to_string(P.ws_bytes) + " bytes");
+    st = check_device();
+    if (st != FCP_OK) return st;
+    st = upload(P.blob, ws, stream);
+    if (st != FCP_OK) return st;
+
+    const fcp::Shape& s = P.shape;
+    const size_t row_bytes = (size_t)s.hkv * s.d * sizeof(uint16_t);
+    const hipMemcpyKind kind =
+        (flags & FCP_PIPE_COPY_SHADER) ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToDeviceNoCU;
+    const bool overlap = copy_stream != stream;
+    // Events: [0] start on stream, then per stage "copied" (on copy_stream) and
+    // "computed" (on stream).
+    std::vector<hipEvent_t> ev;
+    if (overlap) {
+      st = take_sync_events(1 + 2 * (size_t)n_stages, &ev);
+      if (st != FCP_OK) return st;
+    }
+    auto copied = [&](int32_t t) { return ev[1 + 2 * t]; };
+    auto computed = [&](int32_t t) { return ev[2 + 2 * t]; };
+    hipError_t e = hipSuccess;
+    if (overlap) {
+      e = hipEventRecord(ev[0], stream);
+      if (e == hipSuccess) e = hipStreamWaitEvent(copy_stream, ev[0], 0);
+    }
+    for (int32_t t = 0; t < n_stages && e == hipSuccess; ++t) {
+      const int32_t c0 = P.first_copy[t], c1 = P.first_copy[t + 1];
+      if (c1 > c0) {
+        hipStream_t cs = overlap ? copy_stream : stream;
+        if (overlap && t >= 2) e = hipStreamWaitEvent(cs, computed(t - 2), 0);
+        if (e != hipSuccess) break;
+        e = timed(FCP_KERNEL_PIPE_COPY, cs, [&] {
+          hipError_t r = hipSuccess;
+          for (int32_t i = c0; i < c1 && r == hipSuccess; ++i) {
+            const fcp_copy_t& c = copies[i];
+            const size_t dst = (size_t)c.dst_row * row_bytes, src = (size_t)c.src_row * row_bytes;
+            const size_t n = (size_t)c.n_rows * row_bytes;
+            r = hipMemcpyAsync(static_cast<char*>(k) + dst,
+                               static_cast<const char*>(k_src) + src, n, kind, cs);
+            if (r == hipSuccess)
+              r = hipMemcpyAsync(static_cast<char*>(v) + dst,
+                                 static_cast<const char*>(v_src) + src, n, kind, cs);
+          }
+          return r;
+        });
+        if (e != hipSuccess) break;
+        if (overlap) {
+          e = hipEventRecord(copied(t), cs);
+          if (e == hipSuccess) e = hipStreamWaitEvent(stream, copied(t), 0);
+          if (e != hipSuccess) break;
+        }
+      }
+      const fcp::Plan& sp = P.stage[t];
+      if (sp.n_qitems > 0) {
+        void* base = static_cast<char*>(ws) + P.stage_off[t];
+        fcp::FwdArgs a{};
+        a.q = static_cast<const uint16_t*>(q);
+        a.k = static_cast<const uint16_t*>(k);
+        a.v = static_cast<const uint16_t*>(v);
+        a.items = at<fcp::QItem>(base, sp.off_qitems);
+        a.segs = at<fcp::KvSeg>(base, sp.off_segs);
+        a.n_items = sp.n_qitems;
+        a.hq = s.hq, a.hkv = s.hkv, a.group = s.group, a.hpw = s.hpw, a.n_hgroups = s.n_hgroups;
+        a.scale_log2 = s.scale * 1.4426950408889634f;
+        a.o_part = o_part;
+        a.lse_part = lse_part;
+        e = timed(FCP_KERNEL_FWD, stream, [&] { return fcp::launch_fwd(a, s.d, false, stream); });
+        if (e != hipSuccess) break;
+      }
+      if (overlap) e = hipEventRecord(computed(t), stream);
+    }
+    if (e == hipSuccess && P.n_pairs > 0) {
+      void* base = static_cast<char*>(ws) + P.merge_off;
+      fcp::MergeArgs a{};
+      a.o_part = o_part;
+      a.lse_part = lse_part;
+      a.rows = at<fcp::RowItem>(base, P.merge.off_rows);
+      a.parts = at<int32_t>(base, P.merge.off_parts);
+      a.n_rows = P.merge.n_rows;
+      a.hq = s.hq;
+      a.o = static_cast<uint16_t*>(o);
+      a.lse = lse;
+      e = timed(FCP_KERNEL_MERGE, stream, [&] { return fcp::launch_merge(a, s.d, stream); });
+    }
+    if (overlap) give_back_events(ev);
+    return e == hipSuccess ? FCP_OK : hip_err(e, "pipelined forward");
   });
 }
 

@@ -105,16 +105,17 @@ def kv_needs(blocks, q_ids):
 def pull_graph(blocks, assign, n_workers):
     """The block transfers of one causal forward (FCP paper Sec. 4.2, Figure 8): every
     block's K/V live with the worker its Q is assigned to, and every worker pulls each
-    block it needs that another worker holds. Returns (src, dst) int32 arrays, one entry
-    per transfer, sorted by receiver then block id."""
-    src, dst = [], []
+    block it needs that another worker holds. Returns (src, dst, block) int32 arrays, one
+    entry per transfer (sender, receiver, block id), sorted by receiver then block id."""
+    src, dst, blk = [], [], []
     for w in range(n_workers):
         mine = [i for i, a in enumerate(assign) if a == w]
         for j in kv_needs(blocks, mine):
             if assign[j] != w:
                 src.append(assign[j])
                 dst.append(w)
-    return np.asarray(src, dtype=np.int32), np.asarray(dst, dtype=np.int32)
+                blk.append(j)
+    return tuple(np.asarray(x, dtype=np.int32) for x in (src, dst, blk))
 
 
 def zigzag_graph(n_workers=64, seqlen=524288, block=4096):

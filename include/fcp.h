@@ -193,10 +193,63 @@ int fcp_block_attn_bwd(const fcp_dims_t* dims, const void* q, const void* k, con
                        float* dv, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Block-level pipelined forward (FCP paper Sec. 4.2, "Block-level pipelining", Figure 7:
+ * a worker's pull, compute and push are split into block-grained sub-stages that
+ * interleave, each stage's transfer overlapping the previous stage's computation; the
+ * bottom-up coalescer of the same section lets a stage carry c blocks).
+ *
+ * A stage brings KV rows into k / v (the worker's KV buffer, kv_rows rows) by copying
+ * them from k_src / v_src (src_rows rows, same row layout; on one GPU they stand in for
+ * the memory of the workers the blocks are pulled from) and then computes its block
+ * pairs' partials. `stages[s]` takes the next n_copies entries of `copies` and the next
+ * n_pairs entries of `pairs`, in table order. Execution:
+ *  - stage s's copies run on copy_stream after the work enqueued on `stream` before this
+ *    call, and after stage s-2's pairs have been computed (double buffering);
+ *  - stage s's pairs are computed on `stream` (as by fcp_block_attn_fwd: fp32 partials at
+ *    out_row) once stage s's copies are done;
+ *  - after the last stage every pair's partial is merged into o / lse on `stream` (as by
+ *    fcp_merge_partials); `stream` has then also passed every copy.
+ * So the copies of stage s+1 overlap the computation of stage s. The KV rows that stage
+ * s's copies write must not be read by stage s-1's pairs (FCP_ERR_INVALID_ARG otherwise).
+ * copy_stream == stream runs everything in order with no overlap. Copies use a DMA
+ * engine (no compute units) unless flags has FCP_PIPE_COPY_SHADER (copy kernel).
+ * k_src / v_src must not overlap k / v. Tables are host memory read during the call;
+ * o_part / lse_part have dims->part_rows rows; all pairs together must satisfy the
+ * checks of both FCP_OP_FWD and FCP_OP_MERGE. `ws` holds at least
+ * fcp_pipeline_workspace_bytes(...) bytes. A stage may have no copies or no pairs.
+ */
+typedef struct fcp_copy_t {
+  int64_t src_row; /* first row in k_src / v_src */
+  int64_t dst_row; /* first row in k / v */
+  int64_t n_rows;  /* >= 1 */
+} fcp_copy_t;
+
+typedef struct fcp_stage_t {
+  int32_t n_copies;
+  int32_t n_pairs;
+} fcp_stage_t;
+
+#define FCP_PIPE_COPY_SHADER 1
+
+int fcp_pipeline_fwd(const fcp_dims_t* dims, const void* q, void* k, void* v,
+                     const void* k_src, const void* v_src, int64_t src_rows,
+                     const fcp_stage_t* stages, int32_t n_stages, const fcp_copy_t* copies,
+                     const fcp_pair_t* pairs, float* o_part, float* lse_part, void* o,
+                     float* lse, int32_t flags, void* ws, size_t ws_bytes,
+                     hipStream_t stream, hipStream_t copy_stream);
+
+/* Workspace of fcp_pipeline_fwd for these tables (host-only; 0 when invalid, with
+ * fcp_last_error() set, or when there are no pairs). */
+size_t fcp_pipeline_workspace_bytes(const fcp_dims_t* dims, const fcp_stage_t* stages,
+                                    int32_t n_stages, const fcp_copy_t* copies,
+                                    const fcp_pair_t* pairs, int64_t src_rows);
+
+/*
  * Optional per-kernel timing, for measurement tools (not needed for computing).
  * Kernel ids: FCP_KERNEL_FWD (per-pair forward), FCP_KERNEL_FWD_FUSED, FCP_KERNEL_MERGE,
  * FCP_KERNEL_DELTA (backward preprocessing), FCP_KERNEL_DQ, FCP_KERNEL_DKDV,
- * FCP_KERNEL_DKDV_REDUCE (sums the parts of dK/dV tiles the scheduler split by head).
+ * FCP_KERNEL_DKDV_REDUCE (sums the parts of dK/dV tiles the scheduler split by head),
+ * FCP_KERNEL_PIPE_COPY (all copies of one pipeline stage, timed on copy_stream).
  * fcp_timing_enable(1): from now on every kernel launch, from any thread, is bracketed by
  * a pair of HIP events recorded on the call's stream. fcp_timing_enable(0) stops that.
  * fcp_timing_read(): waits for every recorded pair, adds each pair's elapsed time to
@@ -211,7 +264,8 @@ int fcp_block_attn_bwd(const fcp_dims_t* dims, const void* q, const void* k, con
 #define FCP_KERNEL_DQ 4
 #define FCP_KERNEL_DKDV 5
 #define FCP_KERNEL_DKDV_REDUCE 6
-#define FCP_KERNEL_COUNT 7
+#define FCP_KERNEL_PIPE_COPY 7
+#define FCP_KERNEL_COUNT 8
 
 int fcp_timing_enable(int on);
 int fcp_timing_read(double* total_ms, int32_t* launches, int32_t n);

@@ -160,7 +160,7 @@ def test_zigzag_pull_graph(lib):
     needed block it does not hold. Worker 0 needs all 126 remote blocks, and worker 63
     sends its two blocks to 63 + 62 others, so Delta = 2N - 2."""
     n = 64
-    src, dst = W.zigzag_graph(n)
+    src, dst, _ = W.zigzag_graph(n)
     assert len(src) == sum(2 * n - w - 2 for w in range(n))
     stage, k = check_plan(n, src, dst)
     assert k == 2 * n - 2
@@ -170,7 +170,7 @@ def test_zigzag_pull_graph(lib):
 
 def test_heterogeneous_pull_graph(lib):
     """The lognormal batch over 64 workers with its LPT assignment."""
-    src, dst = W.hetero_graph()
+    src, dst, _ = W.hetero_graph()
     stage, k = check_plan(64, src, dst)
     _, kr = C.alternating_path_plan(64, src, dst)
     assert kr == k
@@ -181,7 +181,7 @@ def test_coalesced_stages_stay_balanced(lib, c):
     """Bottom-up coalescing (FCP paper Sec. 4.2): merging c consecutive sub-stages gives
     ceil(Delta / c) stages in which every worker sends and receives at most c blocks."""
     n = 64
-    src, dst = W.zigzag_graph(n)
+    src, dst, _ = W.zigzag_graph(n)
     stage, k = check_plan(n, src, dst)
     coarse = stage // c
     assert coarse.max() + 1 == -(-k // c)
