@@ -58,6 +58,9 @@ def parse():
     return ap.parse_args()
 
 
+PIPE_HEADLINE = "shader_depth3"
+
+
 def pipeline_bench(args):
     """eta of FCP paper Sec. 3.3 on one GPU: time of the pipelined forward of Zig-Zag
     worker 0 of 64 (126 blocks pulled in the congestion-free order, 4 per stage, copies
@@ -84,32 +87,37 @@ def pipeline_bench(args):
             v[t0:t0 + n] = dev["v"][s0:s0 + n]
         return k, v
 
-    pipe = build_pipeline(wl, wl.q_block_ids, recv, coalesce=4)
-    res = build_pipeline(wl, wl.q_block_ids, recv, coalesce=4, slots=None)
+    pipes = {d: build_pipeline(wl, wl.q_block_ids, recv, coalesce=4, depth=d) for d in (2, 3)}
+    res = build_pipeline(wl, wl.q_block_ids, recv, coalesce=4, depth=None)
     # Resident: every stage's blocks already in place, no copies in the tables.
     res_fill = np.concatenate([res["local_copies"], res["copies"]])
     res_stages = res["stages"].copy()
     res_stages["n_copies"] = 0
-    kp, vp = buffers(pipe, pipe["local_copies"])
+    bufs = {d: buffers(P, P["local_copies"]) for d, P in pipes.items()}
     kr, vr = buffers(res, res_fill)
+    pipe = pipes[2]
     o_part = torch.empty((pipe["part_rows"], hq, d), dtype=torch.float32, device="cuda")
     lse_part = torch.empty((pipe["part_rows"], hq), dtype=torch.float32, device="cuda")
     o = torch.empty_like(dev["q"])
     lse = torch.empty((wl.q_rows, hq), dtype=torch.float32, device="cuda")
     cs = torch.cuda.Stream()
     nothing = np.zeros(0, dtype=pipe["copies"].dtype)
+
+    def leg(depth, flags, stream):
+        P, (kp, vp) = pipes[depth], bufs[depth]
+        return lambda: B.fcp_pipeline_fwd(dev["q"], kp, vp, dev["k"], dev["v"], P["stages"],
+                                          P["copies"], P["pairs"], o_part, lse_part, o, lse,
+                                          depth=depth, flags=flags, copy_stream=stream)
+
     legs = {
         "resident": lambda: B.fcp_pipeline_fwd(dev["q"], kr, vr, dev["k"], dev["v"], res_stages,
-                                               nothing, res["pairs"], o_part, lse_part, o, lse),
-        "overlap_dma": lambda: B.fcp_pipeline_fwd(dev["q"], kp, vp, dev["k"], dev["v"],
-                                                  pipe["stages"], pipe["copies"], pipe["pairs"],
-                                                  o_part, lse_part, o, lse, copy_stream=cs),
-        "overlap_shader": lambda: B.fcp_pipeline_fwd(
-            dev["q"], kp, vp, dev["k"], dev["v"], pipe["stages"], pipe["copies"], pipe["pairs"],
-            o_part, lse_part, o, lse, flags=B.FCP_PIPE_COPY_SHADER, copy_stream=cs),
-        "serial_dma": lambda: B.fcp_pipeline_fwd(dev["q"], kp, vp, dev["k"], dev["v"],
-                                                 pipe["stages"], pipe["copies"], pipe["pairs"],
-                                                 o_part, lse_part, o, lse),
+                                               nothing, res["pairs"], o_part, lse_part, o, lse,
+                                               depth=res["depth"]),
+        "dma_depth2": leg(2, 0, cs),
+        "dma_depth3": leg(3, 0, cs),
+        "shader_depth2": leg(2, B.FCP_PIPE_COPY_SHADER, cs),
+        "shader_depth3": leg(3, B.FCP_PIPE_COPY_SHADER, cs),
+        "serial_dma": leg(2, 0, None),
     }
     ms, copy_rate = {}, {}
     copy_bytes = 2 * int(pipe["copies"]["n_rows"].sum()) * hkv * d * 2
@@ -118,13 +126,15 @@ def pipeline_bench(args):
         ms[name], kt = timed(fn, args.steps, args.warmup, True)
         if "pipe_copy" in kt:
             t, n = kt["pipe_copy"]
-            copy_rate[name] = round(copy_bytes * n / args.steps / (t * 1e-3) / 1e9, 1)
+            # bytes over the summed duration of the stages' copy batches
+            copy_rate[name] = round(copy_bytes * args.steps / (t * 1e-3) / 1e9, 1)
     flops = W.fwd_flops(wl)
     result = {
-        "metric": "pipeline_eta", "value": round(ms["overlap_dma"] / ms["resident"], 4),
+        "metric": "pipeline_eta", "value": round(ms[PIPE_HEADLINE] / ms["resident"], 4),
         "unit": "ratio", "higher_is_better": False, "steps": args.steps, "warmup": args.warmup,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": wl.name + "-pipelined", "worker": 0, "n_workers": 64,
+        "config": {"workload": wl.name + "-pipelined", "leg": PIPE_HEADLINE, "worker": 0,
+                   "n_workers": 64,
                    "stages": len(pipe["stages"]), "pulled_blocks": len(recv),
                    "copy_bytes_per_step": copy_bytes},
         "ms_per_step": {k: round(v, 3) for k, v in ms.items()},

@@ -79,8 +79,8 @@ def load():
         "fcp_kernel_name": (ctypes.c_char_p, [ctypes.c_int]),
         "fcp_comm_plan": (ctypes.c_int, [I32, I32, P, P, P, P]),
         "fcp_pipeline_fwd": (ctypes.c_int, [D, P, P, P, P, P, ctypes.c_int64, P, I32, P, P,
-                                            P, P, P, P, I32, P, SZ, P, P]),
-        "fcp_pipeline_workspace_bytes": (SZ, [D, P, I32, P, P, ctypes.c_int64]),
+                                            I32, P, P, P, P, I32, P, SZ, P, P]),
+        "fcp_pipeline_workspace_bytes": (SZ, [D, P, I32, P, P, I32, ctypes.c_int64]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -277,20 +277,21 @@ def _table(x, dtype):
     return arr, arr.ctypes.data_as(ctypes.c_void_p), len(arr)
 
 
-def fcp_pipeline_workspace_bytes(dims, stages, copies, pairs, src_rows):
+def fcp_pipeline_workspace_bytes(dims, stages, copies, pairs, src_rows, depth=2):
     st, sp, ns = _table(stages, STAGE_DTYPE)
     cp, cpp, _ = _table(copies, COPY_DTYPE)
     pr, pp, _ = _table(pairs, PAIR_DTYPE)
-    return load().fcp_pipeline_workspace_bytes(ctypes.byref(dims), sp, ns, cpp, pp,
+    return load().fcp_pipeline_workspace_bytes(ctypes.byref(dims), sp, ns, cpp, pp, int(depth),
                                                int(src_rows))
 
 
 def fcp_pipeline_fwd(q, k, v, k_src, v_src, stages, copies, pairs, o_part, lse_part, o=None,
-                     lse=None, flags=0, softmax_scale=0.0, ws=None, stream=None,
+                     lse=None, depth=2, flags=0, softmax_scale=0.0, ws=None, stream=None,
                      copy_stream=None):
     """Pipelined forward: per stage, copies from k_src/v_src into k/v on ``copy_stream``
-    overlapping the previous stage's pairs on ``stream``; then the merge into o/lse.
-    ``copy_stream=None`` uses ``stream`` (no overlap). k and v are written."""
+    (after stage s-depth has computed) overlapping the pairs of earlier stages on
+    ``stream``; then the merge into o/lse. ``copy_stream=None`` uses ``stream`` (no
+    overlap). k and v are written."""
     import torch
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (k_src, "k_src"), (v_src, "v_src")):
         _need(t, torch.bfloat16, nm)
@@ -311,11 +312,12 @@ def fcp_pipeline_fwd(q, k, v, k_src, v_src, stages, copies, pairs, o_part, lse_p
     lib = load()
     src_rows = k_src.shape[0]
     ws, wsb = _workspace(lambda: lib.fcp_pipeline_workspace_bytes(ctypes.byref(dims), sp, ns,
-                                                                  cpp, pp, src_rows), q, ws)
+                                                                  cpp, pp, int(depth), src_rows),
+                         q, ws)
     s = _stream(q, stream)
     cs = s if copy_stream is None else ctypes.c_void_p(copy_stream.cuda_stream)
     _check(lib.fcp_pipeline_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(k_src),
-                                _ptr(v_src), src_rows, sp, ns, cpp, pp, _ptr(o_part),
+                                _ptr(v_src), src_rows, sp, ns, cpp, pp, int(depth), _ptr(o_part),
                                 _ptr(lse_part), _ptr(o), _ptr(lse), int(flags), _ptr(ws), wsb,
                                 s, cs))
     return o, lse

@@ -442,13 +442,13 @@ int fcp_block_attn_bwd(const fcp_dims_t* dims, const void* q, const void* k, con
 
 size_t fcp_pipeline_workspace_bytes(const fcp_dims_t* dims, const fcp_stage_t* stages,
                                     int32_t n_stages, const fcp_copy_t* copies,
-                                    const fcp_pair_t* pairs, int64_t src_rows) {
+                                    const fcp_pair_t* pairs, int32_t depth, int64_t src_rows) {
   size_t out = 0;
   guarded([&] {
     fcp::PipelinePlan P;
     std::string msg;
-    const int st =
-        fcp::make_pipeline_plan(dims, stages, n_stages, copies, pairs, src_rows, &P, &msg);
+    const int st = fcp::make_pipeline_plan(dims, stages, n_stages, copies, pairs, depth,
+                                           src_rows, &P, &msg);
     if (st != FCP_OK) return set_err(st, msg);
     out = P.ws_bytes;
     return FCP_OK;
@@ -459,14 +459,15 @@ size_t fcp_pipeline_workspace_bytes(const fcp_dims_t* dims, const fcp_stage_t* s
 int fcp_pipeline_fwd(const fcp_dims_t* dims, const void* q, void* k, void* v,
                      const void* k_src, const void* v_src, int64_t src_rows,
                      const fcp_stage_t* stages, int32_t n_stages, const fcp_copy_t* copies,
-                     const fcp_pair_t* pairs, float* o_part, float* lse_part, void* o,
-                     float* lse, int32_t flags, void* ws, size_t ws_bytes,
+                     const fcp_pair_t* pairs, int32_t depth, float* o_part, float* lse_part,
+                     void* o, float* lse, int32_t flags, void* ws, size_t ws_bytes,
                      hipStream_t stream, hipStream_t copy_stream) {
   return guarded([&] {
     if (flags & ~FCP_PIPE_COPY_SHADER) return set_err(FCP_ERR_INVALID_ARG, "unknown flag bits");
     fcp::PipelinePlan P;
     std::string msg;
-    int st = fcp::make_pipeline_plan(dims, stages, n_stages, copies, pairs, src_rows, &P, &msg);
+    int st = fcp::make_pipeline_plan(dims, stages, n_stages, copies, pairs, depth, src_rows,
+                                     &P, &msg);
     if (st != FCP_OK) return set_err(st, msg);
     if (P.n_pairs == 0 && P.n_copies == 0) return FCP_OK;
     st = need_ptrs({k, v});
@@ -504,7 +505,7 @@ int fcp_pipeline_fwd(const fcp_dims_t* dims, const void* q, void* k, void* v,
       const int32_t c0 = P.first_copy[t], c1 = P.first_copy[t + 1];
       if (c1 > c0) {
         hipStream_t cs = overlap ? copy_stream : stream;
-        if (overlap && t >= 2) e = hipStreamWaitEvent(cs, computed(t - 2), 0);
+        if (overlap && t >= depth) e = hipStreamWaitEvent(cs, computed(t - depth), 0);
         if (e != hipSuccess) break;
         e = timed(FCP_KERNEL_PIPE_COPY, cs, [&] {
           hipError_t r = hipSuccess;

@@ -2,9 +2,9 @@
 // pipelining", Figure 7): a worker's computation is split into block-grained stages;
 // while stage s computes, the blocks of stage s+1 are brought in, so communication
 // overlaps computation. Here a stage's "pull" is a device copy of KV rows from a source
-// buffer into the worker's KV buffer. Two stages' KV regions alternate (double
-// buffering): the copies of stage s may overwrite rows that stages up to s-2 read, never
-// rows that stage s-1 reads, because they run while stage s-1 computes.
+// buffer into the worker's KV buffer. The caller rotates through `depth` KV regions: the
+// copies of stage s wait for stage s-depth's computation, so they may overwrite rows that
+// stages up to s-depth read, never rows of stages s-depth+1 .. s-1, which may still run.
 #include "fcp_pipeline.h"
 
 #include <algorithm>
@@ -42,9 +42,10 @@ bool intersects(std::vector<Range> xs, std::vector<Range> ys) {
 }  // namespace
 
 int make_pipeline_plan(const fcp_dims_t* dims, const fcp_stage_t* stages, int32_t n_stages,
-                       const fcp_copy_t* copies, const fcp_pair_t* pairs, int64_t src_rows,
-                       PipelinePlan* P, std::string* err) {
+                       const fcp_copy_t* copies, const fcp_pair_t* pairs, int32_t depth,
+                       int64_t src_rows, PipelinePlan* P, std::string* err) {
   if (!dims) return fail(err, FCP_ERR_INVALID_ARG, "dims is NULL");
+  if (depth < 1) return fail(err, FCP_ERR_INVALID_ARG, "depth must be >= 1");
   if (n_stages < 0) return fail(err, FCP_ERR_INVALID_ARG, "n_stages must be >= 0");
   if (n_stages > 0 && !stages) return fail(err, FCP_ERR_INVALID_ARG, "stages is NULL");
   if (src_rows < 0) return fail(err, FCP_ERR_INVALID_ARG, "src_rows must be >= 0");
@@ -83,17 +84,19 @@ int make_pipeline_plan(const fcp_dims_t* dims, const fcp_stage_t* stages, int32_
                       ", dst " + std::to_string(c.dst_row) + ", rows " +
                       std::to_string(c.n_rows) + "} is empty or out of range");
   }
-  // Double buffering: stage s's copies run while stage s-1 computes.
+  // Stage s's copies may run while stages s-depth+1 .. s-1 compute.
   for (int32_t s = 1; s < n_stages; ++s) {
     std::vector<Range> w, r;
     for (int32_t i = P->first_copy[s]; i < P->first_copy[s + 1]; ++i)
       w.push_back({copies[i].dst_row, copies[i].dst_row + copies[i].n_rows});
-    for (int32_t i = P->first_pair[s - 1]; i < P->first_pair[s]; ++i)
+    if (w.empty()) continue;
+    const int32_t s0 = std::max(0, s - depth + 1);
+    for (int32_t i = P->first_pair[s0]; i < P->first_pair[s]; ++i)
       r.push_back({pairs[i].kv_start, (int64_t)pairs[i].kv_start + pairs[i].kv_len});
     if (intersects(std::move(w), std::move(r)))
       return fail(err, FCP_ERR_INVALID_ARG,
-                  "stage " + std::to_string(s) +
-                      " copies into KV rows that the pairs of the previous stage read");
+                  "stage " + std::to_string(s) + " copies into KV rows that the pairs of one of "
+                      "the previous depth-1 stages read");
   }
 
   // One forward plan per stage, then the merge plan, each at an aligned offset.

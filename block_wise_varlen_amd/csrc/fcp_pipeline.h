@@ -29,7 +29,7 @@ struct PipelinePlan {
 // Validates the stage table, the copies and the pairs; builds one forward plan per stage
 // and the merge plan, laid out back to back in one workspace.
 int make_pipeline_plan(const fcp_dims_t* dims, const fcp_stage_t* stages, int32_t n_stages,
-                       const fcp_copy_t* copies, const fcp_pair_t* pairs, int64_t src_rows,
-                       PipelinePlan* plan, std::string* err);
+                       const fcp_copy_t* copies, const fcp_pair_t* pairs, int32_t depth,
+                       int64_t src_rows, PipelinePlan* plan, std::string* err);
 
 }  // namespace fcp

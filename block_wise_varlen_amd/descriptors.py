@@ -126,7 +126,7 @@ def _stage_pairs(wl, kv_segs, rows):
                 rows.append((qs.seq, qs.row0, qs.length, r0, n, 0, 0, 0))
 
 
-def build_pipeline(wl, local_ids, recv_stage, coalesce=1, slots=2):
+def build_pipeline(wl, local_ids, recv_stage, coalesce=1, depth=3):
     """Tables for ``fcp_pipeline_fwd`` (FCP paper Sec. 4.2: block-level pipelining,
     congestion-free sub-stages, bottom-up coalescing).
 
@@ -137,8 +137,9 @@ def build_pipeline(wl, local_ids, recv_stage, coalesce=1, slots=2):
     ``coalesce`` at a time (coarse stage = sub-stage // coalesce); coarse stages in which
     the worker receives nothing are skipped. Stage 0 computes the local blocks; stage
     t >= 1 copies the blocks of the t-th non-empty coarse stage into a buffer region and
-    computes against them. ``slots`` regions are reused in turn (2: double buffering;
-    None: one region per stage, nothing reused).
+    computes against them. ``depth`` regions are reused in turn (2: double buffering; 3:
+    a copy may start one stage earlier; None: one region per stage, nothing reused);
+    pass the returned ``depth`` to ``fcp_pipeline_fwd``.
 
     The worker's KV buffer holds the local blocks first, then the regions. Returns a dict
     with ``stages``, ``copies`` and ``pairs`` (out_row numbered in table order),
@@ -156,7 +157,7 @@ def build_pipeline(wl, local_ids, recv_stage, coalesce=1, slots=2):
     groups = [sorted(coarse[k], key=lambda i: (int(recv_stage[i]), i)) for k in sorted(coarse)]
     block_rows = lambda i: sum(s.length for s in by_id[i])
     region = max([sum(block_rows(i) for i in g) for g in groups], default=0)
-    n_regions = len(groups) if slots is None else min(slots, len(groups))
+    n_regions = len(groups) if depth is None else min(depth, len(groups))
 
     def placed(blocks_, row):
         """Segments of ``blocks_`` laid out from ``row``, and one copy per block (merged
@@ -192,4 +193,5 @@ def build_pipeline(wl, local_ids, recv_stage, coalesce=1, slots=2):
     return {"stages": np.array(stages, dtype=STAGE_DTYPE), "copies": table(copies),
             "local_copies": table(local_cps),
             "pairs": pairs, "kv_rows": base + n_regions * region, "part_rows": part_rows(pairs),
+            "depth": max(1, n_regions),
             "pulled": [local] + groups}

@@ -202,15 +202,17 @@ int fcp_block_attn_bwd(const fcp_dims_t* dims, const void* q, const void* k, con
  * them from k_src / v_src (src_rows rows, same row layout; on one GPU they stand in for
  * the memory of the workers the blocks are pulled from) and then computes its block
  * pairs' partials. `stages[s]` takes the next n_copies entries of `copies` and the next
- * n_pairs entries of `pairs`, in table order. Execution:
+ * n_pairs entries of `pairs`, in table order. With depth R >= 1 (the number of KV
+ * regions the caller rotates through):
  *  - stage s's copies run on copy_stream after the work enqueued on `stream` before this
- *    call, and after stage s-2's pairs have been computed (double buffering);
+ *    call, and after stage s-R's pairs have been computed;
  *  - stage s's pairs are computed on `stream` (as by fcp_block_attn_fwd: fp32 partials at
  *    out_row) once stage s's copies are done;
  *  - after the last stage every pair's partial is merged into o / lse on `stream` (as by
  *    fcp_merge_partials); `stream` has then also passed every copy.
- * So the copies of stage s+1 overlap the computation of stage s. The KV rows that stage
- * s's copies write must not be read by stage s-1's pairs (FCP_ERR_INVALID_ARG otherwise).
+ * So the copies of stages s+1 .. s+R-1 may overlap the computation of stage s (R = 2:
+ * double buffering). The KV rows that stage s's copies write must not be read by the
+ * pairs of stages s-R+1 .. s-1 (FCP_ERR_INVALID_ARG otherwise).
  * copy_stream == stream runs everything in order with no overlap. Copies use a DMA
  * engine (no compute units) unless flags has FCP_PIPE_COPY_SHADER (copy kernel).
  * k_src / v_src must not overlap k / v. Tables are host memory read during the call;
@@ -234,15 +236,15 @@ typedef struct fcp_stage_t {
 int fcp_pipeline_fwd(const fcp_dims_t* dims, const void* q, void* k, void* v,
                      const void* k_src, const void* v_src, int64_t src_rows,
                      const fcp_stage_t* stages, int32_t n_stages, const fcp_copy_t* copies,
-                     const fcp_pair_t* pairs, float* o_part, float* lse_part, void* o,
-                     float* lse, int32_t flags, void* ws, size_t ws_bytes,
+                     const fcp_pair_t* pairs, int32_t depth, float* o_part, float* lse_part,
+                     void* o, float* lse, int32_t flags, void* ws, size_t ws_bytes,
                      hipStream_t stream, hipStream_t copy_stream);
 
 /* Workspace of fcp_pipeline_fwd for these tables (host-only; 0 when invalid, with
  * fcp_last_error() set, or when there are no pairs). */
 size_t fcp_pipeline_workspace_bytes(const fcp_dims_t* dims, const fcp_stage_t* stages,
                                     int32_t n_stages, const fcp_copy_t* copies,
-                                    const fcp_pair_t* pairs, int64_t src_rows);
+                                    const fcp_pair_t* pairs, int32_t depth, int64_t src_rows);
 
 /*
  * Optional per-kernel timing, for measurement tools (not needed for computing).

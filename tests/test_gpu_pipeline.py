@@ -36,7 +36,7 @@ def packed(seed, causal, hq, hkv, d):
     return wl, local, {int(b): k for k, b in enumerate(order)}
 
 
-def run(wl, dev, P, overlap=True, flags=0):
+def run(wl, dev, P, overlap=True, flags=0, depth=None):
     import torch
     shape = (P["kv_rows"], wl.num_kv_heads, wl.head_dim)
     k = torch.zeros(shape, dtype=torch.bfloat16, device=dev["q"].device)
@@ -51,7 +51,8 @@ def run(wl, dev, P, overlap=True, flags=0):
                            device=k.device)
     cs = torch.cuda.Stream() if overlap else None
     o, lse = B.fcp_pipeline_fwd(dev["q"], k, v, dev["k"], dev["v"], P["stages"], P["copies"],
-                                P["pairs"], o_part, lse_part, flags=flags, copy_stream=cs)
+                                P["pairs"], o_part, lse_part, flags=flags, copy_stream=cs,
+                                depth=P["depth"] if depth is None else depth)
     torch.cuda.synchronize()
     return o, lse
 
@@ -89,7 +90,9 @@ def test_pipeline_modes_bit_identical(gpu, name):
         "serial": run(wl, dev, P, overlap=False),
         "shader-copy": run(wl, dev, P, flags=B.FCP_PIPE_COPY_SHADER),
         "resident": run(wl, dev, build_pipeline(wl, local, recv, coalesce=wl.coalesce,
-                                                 slots=None)),
+                                                 depth=None)),
+        "depth3": run(wl, dev, build_pipeline(wl, local, recv, coalesce=wl.coalesce, depth=3)),
+        "depth1": run(wl, dev, build_pipeline(wl, local, recv, coalesce=wl.coalesce, depth=1)),
     }
     for what, (o, lse) in variants.items():
         assert torch.equal(o, ref[0]) and torch.equal(lse, ref[1]), what
@@ -122,7 +125,7 @@ def test_pipeline_rejects_racing_tables(gpu):
     import torch
     wl, local, recv = CASES["zigzag-N4-w0-c2"]()
     dev, _ = U.inputs(wl, seed=13, which=("q", "k", "v"))
-    P = build_pipeline(wl, local, recv, coalesce=wl.coalesce, slots=1)
-    with pytest.raises(B.FcpError) as e:
-        run(wl, dev, P)
-    assert e.value.status == B.FCP_ERR_INVALID_ARG and "previous stage" in str(e.value)
+    P = build_pipeline(wl, local, recv, coalesce=wl.coalesce, depth=1)
+    with pytest.raises(B.FcpError) as e:   # one region, but two stages in flight
+        run(wl, dev, P, depth=2)
+    assert e.value.status == B.FCP_ERR_INVALID_ARG and "previous" in str(e.value)

@@ -61,11 +61,12 @@ def pipeline_cover(P, wl):
 
 
 def check_double_buffer(P):
+    """Stage t's copies write no row that stages t-depth+1 .. t-1 read."""
     first_c = np.concatenate([[0], np.cumsum(P["stages"]["n_copies"])])
     first_p = np.concatenate([[0], np.cumsum(P["stages"]["n_pairs"])])
     for t in range(1, len(P["stages"])):
         w = P["copies"][first_c[t]:first_c[t + 1]]
-        r = P["pairs"][first_p[t - 1]:first_p[t]]
+        r = P["pairs"][first_p[max(0, t - P["depth"] + 1)]:first_p[t]]
         for c in w:
             for p in r:
                 a0, a1 = c["dst_row"], c["dst_row"] + c["n_rows"]
@@ -75,10 +76,11 @@ def check_double_buffer(P):
 
 @pytest.mark.parametrize("n_workers,block,worker,coalesce,slots", [
     (4, 4, 0, 1, 2), (4, 4, 0, 2, 2), (4, 4, 2, 4, 2), (5, 3, 1, 3, None), (3, 4, 0, 1, None),
+    (5, 4, 0, 1, 3), (4, 4, 0, 1, 1),
 ])
 def test_zigzag_tables_cover_once(lib, n_workers, block, worker, coalesce, slots):
     wl, recv = zigzag_case(n_workers, block, worker, coalesce)
-    P = build_pipeline(wl, wl.q_block_ids, recv, coalesce=coalesce, slots=slots)
+    P = build_pipeline(wl, wl.q_block_ids, recv, coalesce=coalesce, depth=slots)
     cover = pipeline_cover(P, wl)
     assert set(cover) == _true_cover(wl)
     assert all(c == 1 for c in cover.values())
@@ -100,8 +102,8 @@ def test_packed_blocks_tables_cover_once(lib, seed):
     local = [wl.kv_block_ids[0], wl.kv_block_ids[n // 2]]
     order = rng.permutation([i for i in wl.kv_block_ids if i not in local])
     recv = {int(b): k for k, b in enumerate(order)}
-    for slots in (2, None):
-        P = build_pipeline(wl, local, recv, coalesce=2, slots=slots)
+    for slots in (1, 2, 3, None):
+        P = build_pipeline(wl, local, recv, coalesce=2, depth=slots)
         cover = pipeline_cover(P, wl)
         assert set(cover) == _true_cover(wl) and all(c == 1 for c in cover.values())
         check_double_buffer(P)
@@ -109,10 +111,14 @@ def test_packed_blocks_tables_cover_once(lib, seed):
 
 def test_library_accepts_builder_tables(lib):
     wl, recv = zigzag_case(4, 4, 0, 2)
-    P = build_pipeline(wl, wl.q_block_ids, recv, coalesce=2)
+    P = build_pipeline(wl, wl.q_block_ids, recv, coalesce=2, depth=2)
     dims = B.make_dims(2, 1, 64, wl.q_rows, P["kv_rows"], P["part_rows"])
     assert B.fcp_pipeline_workspace_bytes(dims, P["stages"], P["copies"], P["pairs"],
-                                          wl.kv_rows) > 0
+                                          wl.kv_rows, P["depth"]) > 0
+    # The same tables with more stages in flight than regions race.
+    assert B.fcp_pipeline_workspace_bytes(dims, P["stages"], P["copies"], P["pairs"],
+                                          wl.kv_rows, P["depth"] + 1) == 0
+    assert "previous" in B.fcp_last_error()
 
 
 def _tiny_tables():
@@ -128,11 +134,14 @@ def _tiny_tables():
 def test_library_rejects_bad_tables(lib):
     dims, stages, copies, pairs = _tiny_tables()
     assert B.fcp_pipeline_workspace_bytes(dims, stages, copies, pairs, 16) > 0
-    # Stage 1 copies into the rows stage 0 reads: a race with double buffering.
+    # Stage 1 copies into the rows stage 0 reads: a race with double buffering, none
+    # when each stage's copies wait for the previous stage (depth 1).
     bad = copies.copy()
     bad[1]["dst_row"] = 4
     assert B.fcp_pipeline_workspace_bytes(dims, stages, bad, pairs, 16) == 0
-    assert "previous stage" in B.fcp_last_error()
+    assert "previous" in B.fcp_last_error()
+    assert B.fcp_pipeline_workspace_bytes(dims, stages, bad, pairs, 16, depth=1) > 0
+    assert B.fcp_pipeline_workspace_bytes(dims, stages, copies, pairs, 16, depth=0) == 0
     # Copy source or destination out of range, empty copy.
     for field, val in (("src_row", 9), ("dst_row", 9), ("n_rows", 0), ("src_row", -1)):
         bad = copies.copy()
