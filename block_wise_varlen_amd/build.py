@@ -20,7 +20,7 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     # No packed fp32 instructions anywhere in the device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA results in VGPRs; accumulators that live in AGPRs are placed there explicitly.
+    # MFMA accumulators in VGPRs: every kernel runs two waves per SIMD (256 registers each).
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]

@@ -12,12 +12,13 @@
 //    range), like the fused forward. Scores are computed transposed (S^T = K Q^T,
 //    dP^T = V dO^T) so each lane owns a (token, head) column; dQ^T = K^T dS^T takes dS^T
 //    straight from registers and K^T through LDS transpose reads of the K tile.
-//  * dK/dV, KV-stationary: a work item is up to 256 keys of one elementary KV interval
-//    (keys covered by the same set of pairs) for one KV head; it streams every 64-row Q
-//    tile of those pairs and every query head of the group. Scores are computed with
-//    keys as columns (S = Q K^T, dP = dO V^T), so P and dS feed dV^T = dO^T P and
-//    dK^T = Q^T dS from registers, with dO^T and Q^T read by LDS transpose reads of the
-//    row-major Q and dO tiles. K^T is register-resident; the item's V block stays in LDS.
+//  * dK/dV, KV-stationary: a work item is up to 128 keys of one elementary KV interval
+//    (keys covered by the same set of pairs) for one KV head, or a head subset of it; it
+//    streams every 32-row Q tile of those pairs and every query head of the group.
+//    Scores are computed with keys as columns (S = Q K^T, dP = dO V^T) by score waves
+//    that keep K^T and V^T in registers; gradient waves on the same SIMDs take P and dS
+//    through LDS and accumulate dV^T = dO^T P and dK^T = Q^T dS, reading dO^T and Q^T by
+//    LDS transpose reads of the row-major Q and dO tiles.
 // Recomputing S and dP in both kernels costs 4 of the 14 contractions per score; the
 // counted work stays the 5 of the method.
 #include "fcp_common.h"
@@ -207,8 +208,7 @@ void dq_kernel(BwdArgs a) {
 // dK / dV kernel
 // ---------------------------------------------------------------------------------
 
-constexpr int kDkdvWaves = kKvTileBwd / 32;  // 4: one wave per SIMD, 32 keys each
-constexpr int kDkdvRing = 5;                   // Q-tile ring depth
+constexpr int kDkdvWaves = kKvTileBwd / 32;  // 4 SIMD pairs of waves, 32 keys each
 static_assert(kQTileBwd == 32, "one 32-row MFMA block per streamed Q tile");
 
 // First query of segment `s` that sees any key of the item (causal), else 0.
@@ -254,218 +254,228 @@ struct StepCursor {
   }
 };
 
-// 4 waves (one per SIMD), each owning 32 keys as MFMA columns. The wave's K^T and V^T
-// (B operands of S = Q K^T and dP = dO V^T) stay in registers, its dK/dV accumulators in
-// the accumulation registers. Q tiles of 32 rows (with their dO rows and the rows'
-// base-2 LSE and Delta) stream through a 5-deep LDS ring with one barrier per tile.
-// The loop is software-pipelined over tiles: region t interleaves
-//   * the 16 MFMAs of S and dP for tile t + 1 (row reads of its Q and dO),
-//   * the 16 dV^T += dO^T P / dK^T += Q^T dS MFMAs of tile t - 1 (transpose reads),
-//   * the VALU work of tile t: P = exp2(S c - L2), dS = P (dP - Delta), bf16 packing,
-// so the matrix pipe, the VALU and LDS all stay busy from one wave. Ring slots live in
-// region t: t - 1, t, t + 1; t + 2 is landing and t + 3 is issued at the barrier before
-// region t into the slot of t - 2.
+// dK/dV with two waves per SIMD, each pair owning 32 keys as MFMA columns. Waves 0..3 (score waves) own the K^T / V^T
+// registers of their 32 keys and, per tile, compute S and dP, then P and dS (the VALU
+// side), handing P and dS in bf16 to waves 4..7 through LDS. Wave w + 4 runs on wave w's
+// SIMD, owns the same 32 keys and accumulates dV^T += dO^T P and dK^T += Q^T dS for the
+// tile the score wave finished one region earlier; it also issues the ring loads. The
+// matrix pipe of each SIMD thus takes MFMAs from two instruction streams, and one wave's
+// exp / convert / LDS waits no longer stall the other's MFMAs. Q / dO tiles and their
+// (L2, Delta) rows stream through a ring of kDkdvSplitRing slots; all eight waves meet
+// at one barrier per tile. In region t the score waves read tiles t and t + 1, the
+// gradient waves tile t - 1, and tiles up to t + NB - 2 are in flight.
+constexpr int kDkdvSplitWaves = 2 * kDkdvWaves;
+constexpr int kDkdvSplitRing = 6;
+
 template <int D>
-__global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * kDkdvSplitWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void dkdv_split_kernel(BwdArgs a) {
   constexpr int NKC = D / 16;
   constexpr int NDB = D / 32;
   constexpr int NW = kDkdvWaves;
   constexpr int QR = kQTileBwd;
-  constexpr int NB = kDkdvRing;
-  // Loads per wave per tile: Q and dO rows, then one stats load.
-  constexpr int LOADS = 2 * tile_copy_insts<D, QR, NW>() + 1;
+  constexpr int NB = kDkdvSplitRing;
+  constexpr int LOADS = 2 * tile_copy_insts<D, QR, NW>() + 1;  // per tile, per loading wave
   __shared__ __attribute__((aligned(16))) u16 sQ[NB][QR * D];
   __shared__ __attribute__((aligned(16))) u16 sG[NB][QR * D];
-  // Per ring slot and wave: (L2, Delta) of the tile's rows 0..31, interleaved, in the
-  // first 64 of 256 floats (the load writes 16 bytes for each of the 64 lanes).
   __shared__ __attribute__((aligned(16))) float sSt[NB][NW][256];
+  // P (vectors 0, 1) and dS (2, 3) of one tile per SIMD pair, as the B operands of the
+  // gradient MFMAs; two slots, written in region t and read in region t + 1.
+  __shared__ __attribute__((aligned(16))) bf16x8_t sX[2][NW][4][64];
 
   const int item_idx = blockIdx.x / a.hkv;
   const int kvh = blockIdx.x - item_idx * a.hkv;
   const KvItem it = a.kvitems[item_idx];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pw = wave & (NW - 1);  // SIMD pair: keys pw * 32 .. + 31
   const int l32 = lane & 31, hi = lane >> 5;
-  const int64_t kv_stride = (int64_t)a.hkv * D;
-  const int64_t q_stride = (int64_t)a.hq * D;
-  const float c = a.scale_log2;
   const TileOffsets<D> to(lane);
-
-  // This lane's key column; K^T and V^T as B operands (k-slots d = 16*kc + 8*hi + 0..7).
-  const int key = wave * 32 + l32;
+  const int key = pw * 32 + l32;
   const bool kvalid = key < it.kv_rows;
-  const int jkey = it.key_off + key;
-  bf16x8_t kb[NKC], vb[NKC];
-  {
-    const int64_t off = (int64_t)(it.kv_row0 + key) * kv_stride + (int64_t)kvh * D;
-#pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      kb[kc] = kvalid ? *reinterpret_cast<const bf16x8_t*>(a.k + off + 16 * kc + 8 * hi)
-                      : zero_bf16x8();
-      vb[kc] = kvalid ? *reinterpret_cast<const bf16x8_t*>(a.v + off + 16 * kc + 8 * hi)
-                      : zero_bf16x8();
-    }
-  }
-  f32x16_t dk[NDB], dv[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = zero16();
 
   const int seg_end = it.seg_begin + it.seg_count;
-  const int G = a.group;
   const int h_first = it.heads & 0xffff, h_end = h_first + (it.heads >> 16);
   auto advance = [&](const StepCursor& x) {
     return x.next(a.qsegs, it.seg_begin, it.key_off, h_first, h_end);
   };
-  const TileCopy<D, QR, NW> tcopy(q_stride, wave, lane);
-  const uint32_t st_off = lane < 16 ? lane * 16 : 0x7fffffffu;  // lanes past 15: no data
-  auto load = [&](const StepCursor& x, int b) {
-    const int head = kvh * G + x.h;
-    const int64_t col = (int64_t)head * D;
-    const int64_t r0 = (int64_t)x.sg.q_start + x.i0;
-    tcopy(a.q, r0, x.sg.q_len - x.i0, col, sQ[b]);
-    tcopy(a.dout, r0, x.sg.q_len - x.i0, col, sG[b]);
-    // (L2, Delta) of the tile's 32 rows: 256 contiguous bytes, one 16-byte load per lane
-    // for lanes 0..15 (one copy per wave, so every wave counts the same loads); rows past
-    // the range and lanes past 15 read as zero.
-    const uint32_t nbytes = (uint32_t)(min(x.sg.q_len - x.i0, QR) * 8);
-    dma16(buffer_rsrc(a.stats + 2 * (head * a.q_rows + r0), nbytes),
-          lds_addr(&sSt[b][__builtin_amdgcn_readfirstlane(wave)][0]), st_off);
-  };
+  const StepCursor first =
+      StepCursor::last(a.qsegs, it.seg_begin, seg_end - 1, it.key_off, h_first);
+  auto next_slot = [](int b) { return b == NB - 1 ? 0 : b + 1; };
 
-  // Cursors of tiles t + 1, t + 2, t + 3 at region t (tile t's is `cur`).
-  StepCursor cur = StepCursor::last(a.qsegs, it.seg_begin, seg_end - 1, it.key_off, h_first);
-  StepCursor n1 = advance(cur), n2 = advance(n1), n3 = advance(n2);
-  if (cur.valid) load(cur, 0);
-  if (n1.valid) load(n1, 1);
-  if (n2.valid) load(n2, 2);
-  // Tiles 0..2 and the K^T / V^T registers have landed after a full wait, which also
-  // tells the compiler that no load of its own is still pending in the loop.
+  if (wave < NW) {
+    // ---- score waves
+    const float c = a.scale_log2;
+    const int jkey = it.key_off + key;
+    bf16x8_t kb[NKC], vb[NKC];
+    {
+      const int64_t off =
+          (int64_t)(it.kv_row0 + key) * ((int64_t)a.hkv * D) + (int64_t)kvh * D;
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        kb[kc] = kvalid ? *reinterpret_cast<const bf16x8_t*>(a.k + off + 16 * kc + 8 * hi)
+                        : zero_bf16x8();
+        vb[kc] = kvalid ? *reinterpret_cast<const bf16x8_t*>(a.v + off + 16 * kc + 8 * hi)
+                        : zero_bf16x8();
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+
+    StepCursor cur = first;
+    f32x16_t S = zero16(), dP = zero16();
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      S = mfma32(to.rowop(sQ[0], 0, kc), kb[kc], S);
+      dP = mfma32(to.rowop(sG[0], 0, kc), vb[kc], dP);
+    }
+    int buf = 0, x = 0;
+    while (cur.valid) {
+      const int nbuf = next_slot(buf);
+      f32x4_t st[4][2];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float* sp4 = &sSt[buf][pw][16 * g + 8 * hi];
+        st[g][0] = *reinterpret_cast<const f32x4_t*>(sp4);
+        st[g][1] = *reinterpret_cast<const f32x4_t*>(sp4 + 4);
+      }
+      // Causal: query i (within the segment) sees key jkey iff i >= jkey - mask_offset;
+      // rows past the range see nothing. Only tiles on the diagonal or a ragged end mask.
+      {
+        const QSeg sg = cur.sg;
+        const bool causal = sg.flags & 1;
+        const int rows_left = sg.q_len - cur.i0;
+        if ((causal && it.key_off + kKvTileBwd - 1 - sg.mask_offset > cur.i0) || rows_left < QR) {
+          const int lo = causal ? jkey - sg.mask_offset - cur.i0 : -QR;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (row < lo || row >= rows_left) S[r] = -INFINITY;
+          }
+        }
+      }
+      // S and dP of tile t + 1 (row reads PF MFMAs ahead) interleaved with P and dS of
+      // tile t.
+      constexpr int NM = 2 * NKC;
+      constexpr int PF = 2;
+      const u16* Qn = sQ[nbuf];
+      const u16* Gn = sG[nbuf];
+      auto next_op = [&](int n) { return to.rowop((n & 1) ? Gn : Qn, 0, n >> 1); };
+      bf16x8_t an[NM];
+#pragma unroll
+      for (int i = 0; i < PF; ++i) an[i] = next_op(i);
+      f32x16_t Sn = zero16(), dPn = zero16();
+      float p[16], ds[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i < NM) {
+          if (i + PF < NM) an[i + PF] = next_op(i + PF);
+          if (i & 1)
+            dPn = mfma32(an[i], vb[i >> 1], dPn);
+          else
+            Sn = mfma32(an[i], kb[i >> 1], Sn);
+        }
+        const int g = i >> 2, e = i & 3;
+        const float L2 = st[g][e >> 1][2 * (e & 1)];
+        const float Dl = st[g][e >> 1][2 * (e & 1) + 1];
+        p[i] = __builtin_amdgcn_exp2f(fmaf(S[i], c, -L2));
+        ds[i] = p[i] * (dP[i] - Dl);
+      }
+      sX[x][pw][0][lane] = to_bf16x8(p);
+      sX[x][pw][1][lane] = to_bf16x8(p + 8);
+      sX[x][pw][2][lane] = to_bf16x8(ds);
+      sX[x][pw][3][lane] = to_bf16x8(ds + 8);
+      S = Sn;
+      dP = dPn;
+      buf = nbuf;
+      x ^= 1;
+      lds_barrier();
+      cur = advance(cur);
+    }
+    return;
+  }
+
+  // ---- gradient waves: ring loads, then dV / dK.
+  const int G = a.group;
+  const TileCopy<D, QR, NW> tcopy((int64_t)a.hq * D, pw, lane);
+  const uint32_t st_off = lane < 16 ? lane * 16 : 0x7fffffffu;  // lanes past 15: no data
+  auto load = [&](const StepCursor& y, int b) {
+    const int head = kvh * G + y.h;
+    const int64_t col = (int64_t)head * D;
+    const int64_t r0 = (int64_t)y.sg.q_start + y.i0;
+    tcopy(a.q, r0, y.sg.q_len - y.i0, col, sQ[b]);
+    tcopy(a.dout, r0, y.sg.q_len - y.i0, col, sG[b]);
+    // (L2, Delta) of the tile's 32 rows: 256 contiguous bytes, one 16-byte load per lane
+    // for lanes 0..15; rows past the range and lanes past 15 read as zero.
+    const uint32_t nbytes = (uint32_t)(min(y.sg.q_len - y.i0, QR) * 8);
+    dma16(buffer_rsrc(a.stats + 2 * (head * a.q_rows + r0), nbytes),
+          lds_addr(&sSt[b][pw][0]), st_off);
+  };
+  // Cursors of tiles t .. t + NB - 2 in region t.
+  StepCursor cw[NB - 1];
+  cw[0] = first;
+#pragma unroll
+  for (int k = 1; k < NB - 1; ++k) cw[k] = advance(cw[k - 1]);
+#pragma unroll
+  for (int k = 0; k < NB - 2; ++k)
+    if (cw[k].valid) load(cw[k], k);
+  f32x16_t dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = zero16();
   wait_vmem();
   __syncthreads();
-  if (n3.valid) load(n3, 3);
+  if (cw[NB - 2].valid) load(cw[NB - 2], NB - 2);
 
-  auto next_slot = [](int b) { return b == NB - 1 ? 0 : b + 1; };
-  // S and dP of tile t (computed in region t - 1), as MFMA results (rows = queries).
-  f32x16_t S = zero16(), dP = zero16();
-#pragma unroll
-  for (int kc = 0; kc < NKC; ++kc) {
-    S = mfma32(to.rowop(sQ[0], 0, kc), kb[kc], S);
-    dP = mfma32(to.rowop(sG[0], 0, kc), vb[kc], dP);
-  }
-  // P and dS (bf16 B operands) of tile t - 1 and its slot. Before the first tile they
-  // are zeros applied to slot 0 (finite data).
-  bf16x8_t pp[2], sp[2];
-  pp[0] = pp[1] = sp[0] = sp[1] = zero_bf16x8();
-  int pbuf = 0, buf = 0;
-
-  while (cur.valid) {
-    const int nbuf = next_slot(buf);
-    // (L2, Delta) of this lane's rows 8 g + 4 hi + e of tile t.
-    f32x4_t st[4][2];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float* sp4 = &sSt[buf][wave][16 * g + 8 * hi];
-      st[g][0] = *reinterpret_cast<const f32x4_t*>(sp4);
-      st[g][1] = *reinterpret_cast<const f32x4_t*>(sp4 + 4);
-    }
-    // Causal: query i (within the segment) sees key jkey iff i >= jkey - mask_offset;
-    // rows past the range see nothing. Only tiles on the diagonal or a ragged end mask.
-    {
-      const QSeg sg = cur.sg;
-      const bool causal = sg.flags & 1;
-      const int rows_left = sg.q_len - cur.i0;
-      if ((causal && it.key_off + kKvTileBwd - 1 - sg.mask_offset > cur.i0) || rows_left < QR) {
-        const int lo = causal ? jkey - sg.mask_offset - cur.i0 : -QR;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (row < lo || row >= rows_left) S[r] = -INFINITY;
-        }
-      }
-    }
-    // ---- region t. Operand reads run PF MFMAs ahead of their use (LDS latency).
-    constexpr int NM = 2 * NKC;  // MFMAs per stream (S/dP of t + 1; dV/dK of t - 1)
-#ifndef FCP_DKDV_PF
-#define FCP_DKDV_PF 2
-#endif
-    constexpr int PF = FCP_DKDV_PF;
-    static_assert(NM <= 16 && 4 * NDB == NM, "stream lengths");
-    const u16* Qn = sQ[nbuf];
-    const u16* Gn = sG[nbuf];
-    auto next_op = [&](int n) { return to.rowop((n & 1) ? Gn : Qn, 0, n >> 1); };
-    auto prev_op = [&](int n) {
-      return to.trA((n & 1) ? sQ[pbuf] : sG[pbuf], 16 * ((n >> 1) & 1), (n >> 2) * 32);
+  // dV^T += dO^T P and dK^T += Q^T dS for the tile in ring slot b, with P / dS in
+  // exchange slot xs.
+  auto accumulate = [&](int b, int xs) {
+    const bf16x8_t pp0 = sX[xs][pw][0][lane], pp1 = sX[xs][pw][1][lane];
+    const bf16x8_t sp0 = sX[xs][pw][2][lane], sp1 = sX[xs][pw][3][lane];
+    constexpr int NM = 4 * NDB;
+    constexpr int PF = 2;
+    // Operand n: half n / (2 NDB), d block (n / 2) % NDB, dO^T (even) or Q^T (odd).
+    auto op = [&](int n) {
+      const int half = n / (2 * NDB), db = (n >> 1) % NDB;
+      return to.trA((n & 1) ? sQ[b] : sG[b], 16 * half, db * 32);
     };
-    bf16x8_t an[NM], ap[NM];
+    bf16x8_t ap[NM];
 #pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      an[i] = next_op(i);
-      ap[i] = prev_op(i);
-    }
-    f32x16_t Sn = zero16(), dPn = zero16();
-    float p[16], ds[16];
+    for (int i = 0; i < PF; ++i) ap[i] = op(i);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i < NM) {
-        if (i + PF < NM) {
-          an[i + PF] = next_op(i + PF);
-          ap[i + PF] = prev_op(i + PF);
-        }
-        if (i & 1)
-          dPn = mfma32(an[i], vb[i >> 1], dPn);
-        else
-          Sn = mfma32(an[i], kb[i >> 1], Sn);
-        if (i & 1)
-          mfma32_agpr(dk[i >> 2], ap[i], sp[(i >> 1) & 1]);
-        else
-          mfma32_agpr(dv[i >> 2], ap[i], pp[(i >> 1) & 1]);
-      }
-      const int g = i >> 2, e = i & 3;
-      const float L2 = st[g][e >> 1][2 * (e & 1)];
-      const float Dl = st[g][e >> 1][2 * (e & 1) + 1];
-      p[i] = __builtin_amdgcn_exp2f(fmaf(S[i], c, -L2));
-      ds[i] = p[i] * (dP[i] - Dl);
+    for (int i = 0; i < NM; ++i) {
+      if (i + PF < NM) ap[i + PF] = op(i + PF);
+      const int half = i / (2 * NDB), db = (i >> 1) % NDB;
+      if (i & 1)
+        dk[db] = mfma32(ap[i], half ? sp1 : sp0, dk[db]);
+      else
+        dv[db] = mfma32(ap[i], half ? pp1 : pp0, dv[db]);
     }
-    const bf16x8_t pc0 = to_bf16x8(p), pc1 = to_bf16x8(p + 8);
-    const bf16x8_t sc0 = to_bf16x8(ds), sc1 = to_bf16x8(ds + 8);
-    // Keep the conversions in this region rather than sunk past the barrier below.
-    asm volatile("" ::"v"(pc0), "v"(pc1), "v"(sc0), "v"(sc1));
-    pp[0] = pc0;
-    pp[1] = pc1;
-    sp[0] = sc0;
-    sp[1] = sc1;
-    S = Sn;
-    dP = dPn;
+  };
+  int buf = 0, pbuf = 0, x = 0;
+  bool have_prev = false;
+  while (cw[0].valid) {
+    if (have_prev) accumulate(pbuf, x ^ 1);
+    have_prev = true;
     pbuf = buf;
-    buf = nbuf;
-
-    // Barrier before region t + 1: tile t + 2 must have landed (tile t + 3 may still be
-    // in flight), and every wave must be done with the slot of tile t - 1 (read above)
-    // before tile t + 4 is issued into it.
-    if (n3.valid)
+    buf = next_slot(buf);
+    x ^= 1;
+    // Tile t + 2 must have landed; tiles t + 3 .. t + NB - 2 may stay in flight.
+    bool deep = false;
+    if constexpr (NB == 6) deep = cw[4].valid;
+    if (deep)
+      wait_vmem_le<2 * LOADS>();
+    else if (cw[3].valid)
       wait_vmem_le<LOADS>();
     else
       wait_vmem();
     lds_barrier();
-    cur = n1;
-    n1 = n2;
-    n2 = n3;
-    n3 = advance(n3);
-    if (n3.valid) load(n3, (pbuf + NB - 1) % NB);  // the slot of tile t - 1
+#pragma unroll
+    for (int k = 0; k < NB - 2; ++k) cw[k] = cw[k + 1];
+    cw[NB - 2] = advance(cw[NB - 3]);
+    // The slot of tile t - 1 (read above) takes tile t + NB - 1.
+    if (cw[NB - 2].valid) load(cw[NB - 2], (pbuf + NB - 1) % NB);
   }
-  // dV/dK of the last tile.
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      mfma32_agpr(dv[db], to.trA(sG[pbuf], 16 * half, db * 32), pp[half]);
-      mfma32_agpr(dk[db], to.trA(sQ[pbuf], 16 * half, db * 32), sp[half]);
-    }
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    agpr_settle(dk[db]);
-    agpr_settle(dv[db]);
-  }
+  if (have_prev) accumulate(pbuf, x ^ 1);
 
   if (!kvalid) return;
   if (it.slot < 0) {
@@ -545,11 +555,11 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t stream) {
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t stream) {
   if (a.n_kvitems == 0) return hipSuccess;
-  const dim3 grid((unsigned)a.n_kvitems * (unsigned)a.hkv), block(64 * kDkdvWaves);
+  const dim3 grid((unsigned)a.n_kvitems * (unsigned)a.hkv), block(64 * kDkdvSplitWaves);
   if (head_dim == 128)
-    hipLaunchKernelGGL((dkdv_kernel<128>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((dkdv_split_kernel<128>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((dkdv_kernel<64>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((dkdv_split_kernel<64>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

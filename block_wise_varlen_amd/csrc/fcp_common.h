@@ -31,23 +31,6 @@ __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// acc += a * b with the accumulator held in accumulation registers (AGPRs), for
-// long-lived accumulators of kernels that run one wave per SIMD (512 registers, of which
-// only 256 are addressable by VALU instructions). The other MFMAs are compiled in VGPR
-// form (-amdgpu-mfma-vgpr-form), so the compiler never shuffles these accumulators. The
-// two leading wait states cover a VALU write of a or b just before; a run of these
-// MFMAs on one accumulator needs none in between (same-size dependent accumulation).
-// Reading the accumulator with VALU instructions afterwards needs agpr_settle().
-__device__ __forceinline__ void mfma32_agpr(f32x16_t& acc, bf16x8_t a, bf16x8_t b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-
-// Wait states after the last mfma32_agpr on `acc` before its registers are read (a
-// 16-pass MFMA result needs 18; 40 are given).
-__device__ __forceinline__ void agpr_settle(f32x16_t& acc) {
-  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+a"(acc));
-}
-
 __device__ __forceinline__ f32x16_t zero16() {
   f32x16_t z;
 #pragma unroll
