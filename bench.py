@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--workload", default="config2", choices=["config2", "config3", "config4",
                                                               "config5"])
     ap.add_argument("--block", type=int, default=4096, help="block size for config3")
+    ap.add_argument("--coalesce", type=int, default=None,
+                    help="KV blocks coalesced per range for the Zig-Zag (default 4) and "
+                         "heterogeneous (default 1) workloads")
     ap.add_argument("--sweep", dest="sweep", action="store_true", default=True)
     ap.add_argument("--no-sweep", dest="sweep", action="store_false")
     ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false", default=True)
@@ -313,6 +316,27 @@ def roofline(kt, steps, wl, pairs):
             "avg_launch_ms": round(total_ms / launches, 4), "launches": launches}
 
 
+def kernel_rates(kt, wl, pairs):
+    """Achieved rate of every timed kernel against its own roofline: TFLOP/s of counted
+    work for the MFMA kernels, GB/s of algorithmic bytes for the HBM-bound ones."""
+    out = {}
+    for name, (total_ms, launches) in kt.items():
+        try:
+            work, unit, bound = kernel_work(name, wl, pairs)
+        except (KeyError, ValueError):
+            continue
+        if work is None:
+            continue
+        avg_s = total_ms / launches / 1e3
+        if unit == "flop":
+            achieved, peak, u = work / avg_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+        else:
+            achieved, peak, u = work / avg_s / 1e9, PEAK_HBM_GBS, "GB/s"
+        out[name] = {"achieved": round(achieved, 2), "unit": u, "frac": round(achieved / peak, 4),
+                     "bound": bound}
+    return out
+
+
 def calibration_copy(n_bytes=512 << 20, reps=3):
     """A plain device-to-device copy of n_bytes (read n_bytes, write n_bytes per launch),
     whose FETCH_SIZE / WRITE_SIZE counters scale the other kernels' counts to bytes."""
@@ -413,8 +437,8 @@ def main():
 
     wl = {"config2": lambda: W.config2(args.seed),
           "config3": lambda: W.config3(args.block, True),
-          "config4": lambda: W.config4(0),
-          "config5": lambda: W.config5(args.seed)}[args.workload]()
+          "config4": lambda: W.config4(0, coalesce=args.coalesce or 4),
+          "config5": lambda: W.config5(args.seed, coalesce=args.coalesce or 1)}[args.workload]()
     log("workload", wl.name, "q_rows", wl.q_rows, "kv_rows", wl.kv_rows)
     if wl.rng == "host":
         bits = W.make_host_inputs(wl, seed=args.seed)
@@ -443,7 +467,7 @@ def main():
                    "seqlens": wl.seqlens if len(wl.seqlens) <= 16 else len(wl.seqlens),
                    "heads_q": wl.num_q_heads, "heads_kv": wl.num_kv_heads,
                    "head_dim": wl.head_dim, "mask": "causal" if wl.causal else "non-causal",
-                   "pairs": len(pairs), "seed": args.seed,
+                   "pairs": len(pairs), "coalesce": wl.coalesce, "seed": args.seed,
                    "forward": "fused" if args.fused else "partials+merge"},
         "mfu": round(value / PEAK_BF16_TFLOPS, 4),
         "fwd_tflops": round(fl_f / ms_f / 1e9, 2),
@@ -452,6 +476,7 @@ def main():
         "flops_per_step": fl_f + fl_b,
         "kernel_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in kt.items()},
         "roofline": rl,
+        "kernel_rates": kernel_rates(kt, wl, pairs),
         "device": torch.cuda.get_device_name(0),
     }
     log(json.dumps(result))
