@@ -111,6 +111,14 @@ std::vector<Group> group_by_q(const fcp_pair_t* pairs, int n) {
   return out;
 }
 
+// The causal offset of a pair clamped to [-q_len, kv_len]: every offset at or above
+// kv_len - 1 lets each query see every key, every offset at or below -q_len lets none see
+// any, so the clamp keeps the mask and keeps the kernels' int arithmetic on it in range.
+int32_t mask_of(const fcp_pair_t& p) {
+  if (!(p.flags & FCP_PAIR_CAUSAL)) return 0;
+  return std::max(-p.q_len, std::min(p.mask_offset, p.kv_len));
+}
+
 // KV tiles of `kv_len` keys that queries [q_off, q_off + rows) can see.
 int32_t visible_kv_tiles(const KvSeg& s, int32_t q_off, int32_t rows) {
   int64_t last = s.kv_len - 1;
@@ -146,7 +154,7 @@ void group_items(const fcp_pair_t* pairs, const std::vector<Group>& groups, cons
   for (const Group& g : groups) {
     const int32_t sb = (int32_t)segs->size();
     for (int p : g.pairs)
-      segs->push_back(KvSeg{pairs[p].kv_start, pairs[p].kv_len, pairs[p].mask_offset,
+      segs->push_back(KvSeg{pairs[p].kv_start, pairs[p].kv_len, mask_of(pairs[p]),
                             pairs[p].flags});
     for (int32_t t = 0; t < g.q_len; t += s.tile_tokens) {
       QItem it{};
@@ -219,7 +227,7 @@ int make_plan(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t n_pairs, 
     std::vector<KvSeg> segs(n_pairs);
     for (int i = 0; i < n_pairs; ++i) {
       const fcp_pair_t& p = pairs[i];
-      segs[i] = KvSeg{p.kv_start, p.kv_len, p.mask_offset, p.flags};
+      segs[i] = KvSeg{p.kv_start, p.kv_len, mask_of(p), p.flags};
       for (int32_t t = 0; t < p.q_len; t += s.tile_tokens) {
         QItem it{};
         it.q_row0 = p.q_start + t;
@@ -296,7 +304,7 @@ int make_plan(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t n_pairs, 
       const int32_t sb = (int32_t)qsegs.size();
       for (int p : cov)
         qsegs.push_back(QSeg{pairs[p].q_start, pairs[p].q_len,
-                             (int32_t)(pairs[p].mask_offset - (a - pairs[p].kv_start)),
+                             (int32_t)(mask_of(pairs[p]) - (a - pairs[p].kv_start)),
                              pairs[p].flags});
       for (int64_t t = 0; t < b - a; t += kKvTileBwd) {
         KvItem it{};

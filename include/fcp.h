@@ -84,7 +84,8 @@ extern "C" {
  *   mask_offset  in-sequence position of Q row 0 minus that of KV row 0. With the
  *                causal flag, key j (0-based within the pair) is visible to query i iff
  *                j - i <= mask_offset; a query that sees no key of the pair gets an
- *                empty partial (O = 0, LSE = -inf).
+ *                empty partial (O = 0, LSE = -inf). Any int32 value is accepted.
+ *                Ignored without the causal flag.
  *   out_row      first row of this pair's partial in o_part / lse_part (fwd only).
  *   flags        bit 0: causal. Other bits must be zero.
  */
