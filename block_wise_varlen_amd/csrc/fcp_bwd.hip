@@ -354,27 +354,16 @@ void dkdv_split_kernel(BwdArgs a) {
           }
         }
       }
-      // S and dP of tile t + 1 (row reads PF MFMAs ahead) interleaved with P and dS of
-      // tile t.
       constexpr int NM = 2 * NKC;
       constexpr int PF = 2;
       const u16* Qn = sQ[nbuf];
       const u16* Gn = sG[nbuf];
       auto next_op = [&](int n) { return to.rowop((n & 1) ? Gn : Qn, 0, n >> 1); };
-      bf16x8_t an[NM];
-#pragma unroll
-      for (int i = 0; i < PF; ++i) an[i] = next_op(i);
-      f32x16_t Sn = zero16(), dPn = zero16();
+      // P and dS of tile t first, handed over before the S / dP MFMAs of tile t + 1 (row
+      // reads PF MFMAs ahead), which then cover the exchange writes' latency.
       float p[16], ds[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        if (i < NM) {
-          if (i + PF < NM) an[i + PF] = next_op(i + PF);
-          if (i & 1)
-            dPn = mfma32(an[i], vb[i >> 1], dPn);
-          else
-            Sn = mfma32(an[i], kb[i >> 1], Sn);
-        }
         const int g = i >> 2, e = i & 3;
         const float L2 = st[g][e >> 1][2 * (e & 1)];
         const float Dl = st[g][e >> 1][2 * (e & 1) + 1];
@@ -382,9 +371,21 @@ void dkdv_split_kernel(BwdArgs a) {
         ds[i] = p[i] * (dP[i] - Dl);
       }
       sX[x][pw][0][lane] = to_bf16x8(p);
-      sX[x][pw][1][lane] = to_bf16x8(p + 8);
       sX[x][pw][2][lane] = to_bf16x8(ds);
+      sX[x][pw][1][lane] = to_bf16x8(p + 8);
       sX[x][pw][3][lane] = to_bf16x8(ds + 8);
+      bf16x8_t an[NM];
+#pragma unroll
+      for (int i = 0; i < PF; ++i) an[i] = next_op(i);
+      f32x16_t Sn = zero16(), dPn = zero16();
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        if (i + PF < NM) an[i + PF] = next_op(i + PF);
+        if (i & 1)
+          dPn = mfma32(an[i], vb[i >> 1], dPn);
+        else
+          Sn = mfma32(an[i], kb[i >> 1], Sn);
+      }
       S = Sn;
       dP = dPn;
       buf = nbuf;
