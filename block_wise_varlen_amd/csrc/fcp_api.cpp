@@ -320,6 +320,7 @@ int fcp_block_attn_fwd(const fcp_dims_t* dims, const void* q, const void* k, con
     a.v = static_cast<const uint16_t*>(v);
     a.items = at<fcp::QItem>(ws, P.off_qitems);
     a.segs = at<fcp::KvSeg>(ws, P.off_segs);
+    a.seg_out = at<int32_t>(ws, P.off_segout);
     a.n_items = P.n_qitems;
     a.hq = s.hq, a.hkv = s.hkv, a.group = s.group, a.hpw = s.hpw, a.n_hgroups = s.n_hgroups;
     a.scale_log2 = s.scale * 1.4426950408889634f;
@@ -537,6 +538,7 @@ int fcp_pipeline_fwd(const fcp_dims_t* dims, const void* q, void* k, void* v,
         a.v = static_cast<const uint16_t*>(v);
         a.items = at<fcp::QItem>(base, sp.off_qitems);
         a.segs = at<fcp::KvSeg>(base, sp.off_segs);
+        a.seg_out = at<int32_t>(base, sp.off_segout);
         a.n_items = sp.n_qitems;
         a.hq = s.hq, a.hkv = s.hkv, a.group = s.group, a.hpw = s.hpw, a.n_hgroups = s.n_hgroups;
         a.scale_log2 = s.scale * 1.4426950408889634f;

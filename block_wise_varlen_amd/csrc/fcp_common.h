@@ -240,6 +240,13 @@ __device__ __forceinline__ T load_uniform(const T* table, int i) {
   return __builtin_bit_cast(T, t[__builtin_amdgcn_readfirstlane(i)]);
 }
 
+// Entry i of an int32 table, read through the scalar cache (a wave-uniform value).
+__device__ __forceinline__ int32_t load_uniform_i32(const int32_t* table, int i) {
+  const __attribute__((address_space(4))) int32_t* t =
+      (const __attribute__((address_space(4))) int32_t*)table;
+  return t[__builtin_amdgcn_readfirstlane(i)];
+}
+
 // Waits for this wave's outstanding vector-memory operations (the async tile copies).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
 

@@ -145,6 +145,49 @@ void fwd_kernel(FwdArgs a) {
       for (int cb = 0; cb < CB; ++cb) S[cb] = mfma32(kk, qb[cb][kc], S[cb]);
     }
   }
+  // Writes this item's rows of one output: O = acc / l, LSE = (m + log2 l) ln 2; no
+  // visible key (or `empty`) -> O = 0, LSE = -inf. row0: output row of query tok 0.
+  auto store = [&](int64_t row0, bool empty) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const float lt = empty ? 0.f : pair_sum(l[cb]);
+      if (!valid[cb]) continue;
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const float lse = lt > 0.f ? (m[cb] + __log2f(lt)) * kLn2 : -INFINITY;
+      const int64_t row = row0 + tok[cb];
+      const int64_t base = (row * a.hq + head[cb]) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = db * 32 + 8 * g4 + 4 * hi;
+          const float o0 = empty ? 0.f : acc[cb][db][4 * g4 + 0] * inv;
+          const float o1 = empty ? 0.f : acc[cb][db][4 * g4 + 1] * inv;
+          const float o2 = empty ? 0.f : acc[cb][db][4 * g4 + 2] * inv;
+          const float o3 = empty ? 0.f : acc[cb][db][4 * g4 + 3] * inv;
+          if constexpr (FINAL) {
+            const uint32_t w0 = (uint32_t)f32_to_bf16(o0) | ((uint32_t)f32_to_bf16(o1) << 16);
+            const uint32_t w1 = (uint32_t)f32_to_bf16(o2) | ((uint32_t)f32_to_bf16(o3) << 16);
+            *reinterpret_cast<u32x2_t*>(a.o + base + d) = u32x2_t{w0, w1};
+          } else {
+            *reinterpret_cast<f32x4_t*>(a.o_part + base + d) = f32x4_t{o0, o1, o2, o3};
+          }
+        }
+      if (hi == 0) {
+        if constexpr (FINAL)
+          a.lse[row * a.hq + head[cb]] = lse;
+        else
+          a.lse_part[row * a.hq + head[cb]] = lse;
+      }
+    }
+  };
+  // Per-pair partials: each KV segment is one pair with its own partial rows. seg_cur is
+  // the segment being accumulated; segments without a visible tile get empty partials.
+  auto part_row0 = [&](int sidx) { return (int64_t)load_uniform_i32(a.seg_out, sidx) + it.q_off; };
+  int seg_cur = cur.valid ? cur.s : seg_end;
+  if constexpr (!FINAL)
+    for (int s2 = it.seg_begin; s2 < seg_cur; ++s2) store(part_row0(s2), true);
+
   int buf = 0;
   bool first_tile = true;
 
@@ -156,6 +199,9 @@ void fwd_kernel(FwdArgs a) {
       copy(nx, buf ^ 1);
     }
     const KvSeg sg = cur.sg;
+    // Per-pair partials: this tile starts a new pair, whose predecessor is complete once
+    // the first block's pending PV (the predecessor's last block) has been added.
+    const bool boundary = !FINAL && cur.s != seg_cur;
     const int j0 = cur.t * kFwdKt;
     const bool causal = sg.flags & 1;
     const bool need_mask = (j0 + kFwdKt > sg.kv_len) ||
@@ -192,6 +238,20 @@ void fwd_kernel(FwdArgs a) {
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb)
             acc[cb][db] = mfma32(va[2 * db + half], pb[cb][half], acc[cb][db]);
+      if constexpr (!FINAL) {
+        if (kb == 0 && boundary) {
+          store(part_row0(seg_cur), false);
+          for (int s2 = seg_cur + 1; s2 < cur.s; ++s2) store(part_row0(s2), true);
+          seg_cur = cur.s;
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) {
+            m[cb] = -INFINITY;
+            l[cb] = 0.f;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) acc[cb][db] = zero16();
+          }
+        }
+      }
       {
         const u16* kt = kb + 1 < NKB ? Kt : Kn;
         const int kr = kb + 1 < NKB ? (kb + 1) * 32 : 0;
@@ -283,36 +343,11 @@ void fwd_kernel(FwdArgs a) {
       for (int cb = 0; cb < CB; ++cb)
         acc[cb][db] = mfma32(va[2 * db + half], pb[cb][half], acc[cb][db]);
 
-  // Epilogue: O = acc / l, LSE = (m + log2 l) ln 2; no visible key -> O = 0, LSE = -inf.
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    const float lt = pair_sum(l[cb]);
-    if (!valid[cb]) continue;
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float lse = lt > 0.f ? (m[cb] + __log2f(lt)) * kLn2 : -INFINITY;
-    const int64_t row = it.out_row0 + tok[cb];
-    const int64_t base = (row * a.hq + head[cb]) * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = db * 32 + 8 * g4 + 4 * hi;
-        const float o0 = acc[cb][db][4 * g4 + 0] * inv, o1 = acc[cb][db][4 * g4 + 1] * inv;
-        const float o2 = acc[cb][db][4 * g4 + 2] * inv, o3 = acc[cb][db][4 * g4 + 3] * inv;
-        if constexpr (FINAL) {
-          const uint32_t w0 = (uint32_t)f32_to_bf16(o0) | ((uint32_t)f32_to_bf16(o1) << 16);
-          const uint32_t w1 = (uint32_t)f32_to_bf16(o2) | ((uint32_t)f32_to_bf16(o3) << 16);
-          *reinterpret_cast<u32x2_t*>(a.o + base + d) = u32x2_t{w0, w1};
-        } else {
-          *reinterpret_cast<f32x4_t*>(a.o_part + base + d) = f32x4_t{o0, o1, o2, o3};
-        }
-      }
-    if (hi == 0) {
-      if constexpr (FINAL)
-        a.lse[row * a.hq + head[cb]] = lse;
-      else
-        a.lse_part[row * a.hq + head[cb]] = lse;
-    }
+  if constexpr (FINAL) {
+    store(it.out_row0, false);
+  } else {
+    if (seg_cur < seg_end) store(part_row0(seg_cur), false);
+    for (int s2 = seg_cur + 1; s2 < seg_end; ++s2) store(part_row0(s2), true);
   }
 }
 

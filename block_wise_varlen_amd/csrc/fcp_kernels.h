@@ -14,6 +14,7 @@ struct FwdArgs {
   const uint16_t* v;   // bf16 [kv_rows, hkv, D]
   const QItem* items;  // n_items, in launch order
   const KvSeg* segs;
+  const int32_t* seg_out;  // per-pair mode: partial row of each KvSeg's first query
   int n_items;
   int hq, hkv, group, hpw, n_hgroups;
   float scale_log2;  // softmax scale * log2(e)

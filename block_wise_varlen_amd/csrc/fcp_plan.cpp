@@ -148,14 +148,18 @@ void sort_heaviest_first(std::vector<QItem>* items) {
                    [](const QItem& a, const QItem& b) { return a.cost > b.cost; });
 }
 
-// Q-stationary items over groups of identical Q range (fused forward and dQ).
+// Q-stationary items over groups of identical Q range (both forwards and dQ). With
+// seg_out, also records each segment's pair's first partial-output row.
 void group_items(const fcp_pair_t* pairs, const std::vector<Group>& groups, const Shape& s,
-                 std::vector<QItem>* items, std::vector<KvSeg>* segs) {
+                 std::vector<QItem>* items, std::vector<KvSeg>* segs,
+                 std::vector<int32_t>* seg_out = nullptr) {
   for (const Group& g : groups) {
     const int32_t sb = (int32_t)segs->size();
-    for (int p : g.pairs)
+    for (int p : g.pairs) {
       segs->push_back(KvSeg{pairs[p].kv_start, pairs[p].kv_len, mask_of(pairs[p]),
                             pairs[p].flags});
+      if (seg_out) seg_out->push_back(pairs[p].out_row);
+    }
     for (int32_t t = 0; t < g.q_len; t += s.tile_tokens) {
       QItem it{};
       it.q_row0 = g.q_start + t;
@@ -223,26 +227,15 @@ int make_plan(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t n_pairs, 
   if (n_pairs == 0) return FCP_OK;
 
   if (op == FCP_OP_FWD) {
+    // One item per tile of a Q range walks every pair of that range, as the fused
+    // forward does, and writes each pair's partial where the pair ends.
     std::vector<QItem> items;
-    std::vector<KvSeg> segs(n_pairs);
-    for (int i = 0; i < n_pairs; ++i) {
-      const fcp_pair_t& p = pairs[i];
-      segs[i] = KvSeg{p.kv_start, p.kv_len, mask_of(p), p.flags};
-      for (int32_t t = 0; t < p.q_len; t += s.tile_tokens) {
-        QItem it{};
-        it.q_row0 = p.q_start + t;
-        it.q_rows = std::min(s.tile_tokens, p.q_len - t);
-        it.q_off = t;
-        it.out_row0 = p.out_row + t;
-        it.seg_begin = i;
-        it.seg_count = 1;
-        it.cost = visible_kv_tiles(segs[i], t, it.q_rows);
-        items.push_back(it);
-      }
-    }
-    sort_heaviest_first(&items);
+    std::vector<KvSeg> segs;
+    std::vector<int32_t> seg_out;
+    group_items(pairs, group_by_q(pairs, n_pairs), s, &items, &segs, &seg_out);
     P.off_qitems = put(&P.blob, items);
     P.off_segs = put(&P.blob, segs);
+    P.off_segout = put(&P.blob, seg_out);
     P.n_qitems = (int)items.size();
   } else if (op == FCP_OP_FWD_FUSED) {
     std::vector<QItem> items;
