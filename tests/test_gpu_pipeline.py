@@ -121,6 +121,36 @@ def test_pipeline_full_size_zigzag(gpu):
                  o_ref, l_ref, "zigzag pipeline")
 
 
+def test_pipeline_full_size_heterogeneous(gpu):
+    """The heaviest worker of the heterogeneous lognormal batch (64 workers, 4K blocks,
+    packed short sequences, LPT): the KV blocks it does not hold are pulled in the
+    congestion-free order of the whole batch's pull graph, 4 sub-stages per stage;
+    sampled rows against the oracle."""
+    import torch
+    wl = W.config5(0)
+    src, dst, blk = W.hetero_graph()
+    stage, _ = B.fcp_comm_plan(64, src, dst)
+    w = wl.meta["worker"]
+    m = dst == w
+    recv = {int(b): int(s) for b, s in zip(blk[m], stage[m])}
+    local = [i for i in wl.kv_block_ids if wl.meta["assign"][i] == w]
+    assert set(recv) == set(wl.kv_block_ids) - set(local)
+    P = build_pipeline(wl, local, recv, coalesce=4)
+    print("stages", len(P["stages"]), "pairs", len(P["pairs"]), flush=True)
+    dev = W.make_device_inputs(wl, seed=0, which=("q", "k", "v"))
+    o, lse = run(wl, dev, P)
+    rng = np.random.default_rng(5)
+    rows = U.sample_rows(wl, 12, seed=5)
+    if len(rows) > 40:
+        rows = np.sort(rng.choice(rows, 40, replace=False))
+    idx = oracle.SeqIndex(wl)
+    o_ref, l_ref = oracle.forward(U.DeviceRows(dev["q"]), U.DeviceRows(dev["k"]),
+                                  U.DeviceRows(dev["v"]), idx, rows=rows)
+    ridx = torch.as_tensor(rows, device=o.device)
+    U.check_attn(U.bf16_to_f64(o.index_select(0, ridx)), lse.index_select(0, ridx).cpu().numpy(),
+                 o_ref, l_ref, "heterogeneous pipeline")
+
+
 def test_pipeline_rejects_racing_tables(gpu):
     import torch
     wl, local, recv = CASES["zigzag-N4-w0-c2"]()
