@@ -343,11 +343,18 @@ def calibration_copy(n_bytes=512 << 20, reps=3):
     import torch
     src = torch.empty(n_bytes, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
     for _ in range(reps):
         dst.copy_(src)
+    e1.record()
     torch.cuda.synchronize()
-    log("calibration copy: %d bytes read and %d bytes written per launch, %d launches"
-        % (n_bytes, n_bytes, reps))
+    ms = e0.elapsed_time(e1) / reps
+    log("calibration copy: %d bytes read and %d bytes written per launch, %d launches, "
+        "%.3f ms each = %.0f GB/s read+write" % (n_bytes, n_bytes, reps + 1, ms,
+                                                 2 * n_bytes / ms / 1e6))
 
 
 def cpu_baseline(wl, seed):
