@@ -133,14 +133,28 @@ void dq_kernel(BwdArgs a) {
       f32x16_t S[CB], dP[CB];
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) S[cb] = dP[cb] = zero16();
+      // S^T and dP^T: operand rows are read PF MFMAs ahead; the scheduling barriers keep
+      // that order (left alone, the compiler reads each operand one MFMA ahead and every
+      // MFMA waits for LDS).
+      {
+        constexpr int NM = 2 * NKC, PF = 4;
+        auto op = [&](int i) { return to.rowop((i & 1) ? Vt : Kt, kb * 32, i >> 1); };
+        bf16x8_t ops[NM];
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        const bf16x8_t ka = to.rowop(Kt, kb * 32, kc);
-        const bf16x8_t va = to.rowop(Vt, kb * 32, kc);
+        for (int i = 0; i < PF; ++i) ops[i] = op(i);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          S[cb] = mfma32(ka, qb[cb][kc], S[cb]);
-          dP[cb] = mfma32(va, gb[cb][kc], dP[cb]);
+        for (int i = 0; i < NM; ++i) {
+          if (i + PF < NM) ops[i + PF] = op(i + PF);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) {
+            if (i & 1)
+              dP[cb] = mfma32(ops[i], gb[cb][i >> 1], dP[cb]);
+            else
+              S[cb] = mfma32(ops[i], qb[cb][i >> 1], S[cb]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       bf16x8_t dsb[CB][2];
@@ -160,14 +174,23 @@ void dq_kernel(BwdArgs a) {
         dsb[cb][1] = to_bf16x8(ds + 8);
       }
       // dQ^T += K^T dS^T (contraction over the block's 32 keys).
+      {
+        constexpr int NT = 2 * NDB, PT = 2;
+        auto top = [&](int i) { return to.trA(Kt, kb * 32 + 16 * (i & 1), (i >> 1) * 32); };
+        bf16x8_t kts[NT];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+        for (int i = 0; i < PT; ++i) kts[i] = top(i);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const bf16x8_t kt = to.trA(Kt, kb * 32 + 16 * half, db * 32);
+        for (int i = 0; i < NT; ++i) {
+          if (i + PT < NT) kts[i + PT] = top(i + PT);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int cb = 0; cb < CB; ++cb) acc[cb][db] = mfma32(kt, dsb[cb][half], acc[cb][db]);
+          for (int cb = 0; cb < CB; ++cb)
+            acc[cb][i >> 1] = mfma32(kts[i], dsb[cb][i & 1], acc[cb][i >> 1]);
+          __builtin_amdgcn_sched_barrier(0);
         }
+      }
     }
 
     // Tile t + 1 must have landed (t + 2 and t + 3 may stay in flight) before the
@@ -432,8 +455,10 @@ void dkdv_split_kernel(BwdArgs a) {
   auto accumulate = [&](int b, int xs) {
     const bf16x8_t pp0 = sX[xs][pw][0][lane], pp1 = sX[xs][pw][1][lane];
     const bf16x8_t sp0 = sX[xs][pw][2][lane], sp1 = sX[xs][pw][3][lane];
+    // Transpose operands PF MFMAs ahead, the order kept by scheduling barriers (the
+    // compiler alone reads one operand ahead).
     constexpr int NM = 4 * NDB;
-    constexpr int PF = 2;
+    constexpr int PF = 3;
     // Operand n: half n / (2 NDB), d block (n / 2) % NDB, dO^T (even) or Q^T (odd).
     auto op = [&](int n) {
       const int half = n / (2 * NDB), db = (n >> 1) % NDB;
@@ -442,14 +467,17 @@ void dkdv_split_kernel(BwdArgs a) {
     bf16x8_t ap[NM];
 #pragma unroll
     for (int i = 0; i < PF; ++i) ap[i] = op(i);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       if (i + PF < NM) ap[i + PF] = op(i + PF);
+      __builtin_amdgcn_sched_barrier(0);
       const int half = i / (2 * NDB), db = (i >> 1) % NDB;
       if (i & 1)
         dk[db] = mfma32(ap[i], half ? sp1 : sp0, dk[db]);
       else
         dv[db] = mfma32(ap[i], half ? pp1 : pp0, dv[db]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   int buf = 0, pbuf = 0, x = 0;
