@@ -21,8 +21,9 @@
 //  * The running max is only raised (and the accumulator rescaled) when a new score
 //    exceeds it by more than 2^8, so in steady state the accumulator is touched by MFMAs
 //    only; P <= 2^8 meanwhile, which bf16 and fp32 hold exactly as well as P <= 1.
-//  * K/V tiles of 64 keys go through a 3-deep LDS ring: the copy of tile n+2 is issued
-//    before the MFMAs of tile n, and tile n+1 is waited for at the end of the iteration.
+//  * K/V tiles of 128 keys go through a 2-slot LDS ring: the copy of tile n+1 is issued
+//    once every wave has left tile n-1's slot, and is waited for before the last 32-key
+//    block of tile n (whose QK^T reads tile n+1's first keys).
 #include "fcp_common.h"
 #include "fcp_cursor.h"
 #include "fcp_kernels.h"
@@ -190,6 +191,12 @@ void fwd_kernel(FwdArgs a) {
 
   int buf = 0;
   bool first_tile = true;
+  // A store() issues 4 * NDB 16-byte stores per column block whose lane 0 holds a valid
+  // row (the compiler skips the block only when no lane of the wave is valid), plus the
+  // LSE store. kBurstStores counts the O stores of the wave's first column block: the
+  // smallest number a store() of this wave issues, or 0 when it issues none.
+  constexpr int kBurstStores = 4 * NDB;
+  const bool wave_stores = (wave * CB / a.hpw) * kColBlock < it.q_rows;
 
   while (cur.valid) {
     // Tile n + 1 goes into the slot of tile n - 1, whose last reads (the V^T operands of
@@ -202,6 +209,8 @@ void fwd_kernel(FwdArgs a) {
     // Per-pair partials: this tile starts a new pair, whose predecessor is complete once
     // the first block's pending PV (the predecessor's last block) has been added.
     const bool boundary = !FINAL && cur.s != seg_cur;
+    // The partial stores of a boundary come after this tile's copy of the next tile.
+    const bool burst_after_copy = boundary && !first_tile && wave_stores;
     const int j0 = cur.t * kFwdKt;
     const bool causal = sg.flags & 1;
     const bool need_mask = (j0 + kFwdKt > sg.kv_len) ||
@@ -213,8 +222,14 @@ void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       if (kb == NKB - 1 && nx.valid) {
-        // The next tile's K is read from here on.
-        wait_vmem();
+        // The next tile's K is read from here on. Vector-memory operations retire in issue
+        // order, so when this wave stored a finished partial after issuing that tile's
+        // copy, waiting until only those stores are outstanding suffices: the partial
+        // drains to memory while the next tile is computed.
+        if (burst_after_copy)
+          wait_vmem_le<kBurstStores>();
+        else
+          wait_vmem();
         lds_barrier();
       }
       if (need_mask) {
