@@ -391,25 +391,14 @@ int fcp_block_attn_bwd(const fcp_dims_t* dims, const void* q, const void* k, con
                      ws_bytes, stream, &P);
     if (st != FCP_OK || n_pairs == 0) return st;
     const fcp::Shape& s = P.shape;
-    float* stats = reinterpret_cast<float*>(static_cast<char*>(ws) + P.off_delta);
-    fcp::DeltaArgs da{};
-    da.o = static_cast<const uint16_t*>(o);
-    da.dout = static_cast<const uint16_t*>(dout);
-    da.lse = lse;
-    da.rows = at<fcp::RowItem>(ws, P.off_rows);
-    da.n_rows = P.n_rows;
-    da.hq = s.hq;
-    da.stats = stats;
-    da.q_rows = dims->q_rows;
-    hipError_t e =
-        timed(FCP_KERNEL_DELTA, stream, [&] { return fcp::launch_delta(da, s.d, stream); });
-    if (e != hipSuccess) return hip_err(e, "delta launch");
     fcp::BwdArgs a{};
     a.q = static_cast<const uint16_t*>(q);
     a.k = static_cast<const uint16_t*>(k);
     a.v = static_cast<const uint16_t*>(v);
     a.dout = static_cast<const uint16_t*>(dout);
-    a.stats = stats;
+    a.o = static_cast<const uint16_t*>(o);
+    a.lse = lse;
+    a.stats = reinterpret_cast<float*>(static_cast<char*>(ws) + P.off_stats);
     a.q_rows = dims->q_rows;
     a.qitems = at<fcp::QItem>(ws, P.off_qitems);
     a.segs = at<fcp::KvSeg>(ws, P.off_segs);
@@ -428,7 +417,8 @@ int fcp_block_attn_bwd(const fcp_dims_t* dims, const void* q, const void* k, con
     a.part_dv = a.part_dk + part_floats;
     a.reduce = at<fcp::ReduceItem>(ws, P.off_reduce);
     a.n_reduce = P.n_reduce;
-    e = timed(FCP_KERNEL_DQ, stream, [&] { return fcp::launch_bwd_dq(a, s.d, stream); });
+    hipError_t e =
+        timed(FCP_KERNEL_DQ, stream, [&] { return fcp::launch_bwd_dq(a, s.d, stream); });
     if (e != hipSuccess) return hip_err(e, "dQ launch");
     e = timed(FCP_KERNEL_DKDV, stream, [&] { return fcp::launch_bwd_dkdv(a, s.d, stream); });
     if (e != hipSuccess) return hip_err(e, "dK/dV launch");

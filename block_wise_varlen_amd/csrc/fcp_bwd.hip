@@ -11,7 +11,9 @@
 //  * dQ, Q-stationary: a work item is a tile of rows of one Q range (all pairs of that
 //    range), like the fused forward. Scores are computed transposed (S^T = K Q^T,
 //    dP^T = V dO^T) so each lane owns a (token, head) column; dQ^T = K^T dS^T takes dS^T
-//    straight from registers and K^T through LDS transpose reads of the K tile.
+//    straight from registers and K^T through LDS transpose reads of the K tile. Every
+//    (row, head) belongs to exactly one dQ item, which also computes its Delta and stores
+//    it with the LSE as the row statistics the dK/dV kernel reads.
 //  * dK/dV, KV-stationary: a work item is up to 128 keys of one elementary KV interval
 //    (keys covered by the same set of pairs) for one KV head, or a head subset of it; it
 //    streams every 32-row Q tile of those pairs and every query head of the group.
@@ -80,13 +82,30 @@ void dq_kernel(BwdArgs a) {
       gb[cb][kc] = valid[cb] ? *reinterpret_cast<const bf16x8_t*>(grow + 16 * kc + 8 * hi)
                              : zero_bf16x8();
     }
-    // Rows with LSE = -inf (or padding rows) get P = 0 through an infinite shift.
-    const f32x2_t st = valid[cb] ? *reinterpret_cast<const f32x2_t*>(
-                                       a.stats + 2 * (head[cb] * a.q_rows + row))
-                                 : f32x2_t{INFINITY, 0.f};
-    lse2[cb] = st[0];
-    dlt[cb] = st[1];
+    // Delta = dO . O over this lane's half of the head dimension (the same k-slots as its
+    // dO^T registers), then over both halves; fp32 from the bf16 tensors.
+    const u16* orow = a.o + row * q_stride + (int64_t)head[cb] * D;
+    float dl = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      const bf16x8_t ob = valid[cb] ? *reinterpret_cast<const bf16x8_t*>(orow + 16 * kc + 8 * hi)
+                                    : zero_bf16x8();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dl = fmaf((float)ob[i], (float)gb[cb][kc][i], dl);
+    }
+    dlt[cb] = pair_sum(dl);
+    // LSE in base 2; rows with LSE = -inf (or padding rows) get P = 0 through an infinite
+    // shift.
+    const float L = valid[cb] ? a.lse[row * a.hq + head[cb]] : -INFINITY;
+    lse2[cb] = L == -INFINITY ? INFINITY : L * kLog2e;
   }
+
+  // Row statistics (LSE in base 2, Delta) for the dK/dV kernel, head-major.
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+    if (valid[cb] && hi == 0)
+      *reinterpret_cast<f32x2_t*>(a.stats + 2 * (head[cb] * a.q_rows + it.q_row0 + tok[cb])) =
+          f32x2_t{lse2[cb], dlt[cb]};
 
   f32x16_t acc[CB][NDB];
 #pragma unroll

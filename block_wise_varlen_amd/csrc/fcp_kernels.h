@@ -35,23 +35,14 @@ struct MergeArgs {
   float* lse;   // fp32 [q_rows, hq]
 };
 
-struct DeltaArgs {
-  const uint16_t* o;     // bf16 merged output
-  const uint16_t* dout;  // bf16 upstream gradient
-  const float* lse;      // fp32 [q_rows, hq], natural log
-  const RowItem* rows;
-  int n_rows;
-  int hq;
-  float* stats;  // fp32 [hq, q_rows, 2]: LSE * log2(e) (+inf where LSE = -inf), Delta
-  int64_t q_rows;
-};
-
 struct BwdArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dout;
-  const float* stats;  // fp32 [hq, q_rows, 2] from the Delta kernel
+  const uint16_t* o;   // bf16 merged output
+  const float* lse;    // fp32 [q_rows, hq] merged LSE, natural log
+  float* stats;        // fp32 [hq, q_rows, 2]: written by the dQ kernel, read by dK/dV
   int64_t q_rows;
   const QItem* qitems;
   const KvSeg* segs;
@@ -72,7 +63,6 @@ struct BwdArgs {
 
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool final_out, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
-hipError_t launch_delta(const DeltaArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_reduce(const BwdArgs& a, int head_dim, hipStream_t stream);

@@ -1,6 +1,6 @@
-// Streaming kernels: the LSE merge of per-pair partials and the backward's per-row
-// Delta = sum_d dO * O. Both are bound by HBM bandwidth; one workgroup handles one query
-// row across all heads so that every partial row is read as one contiguous run.
+// Streaming kernel: the LSE merge of per-pair partials, bound by HBM bandwidth; one
+// workgroup handles one query row across all heads so that every partial row is read as
+// one contiguous run.
 //
 // Merge (FCP paper Sec. 2.2: per-slice results of a sequence reduce to the final output;
 // the reduction is the log-sum-exp combine): for every head,
@@ -70,40 +70,6 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   }
 }
 
-// Delta_i = sum_d dO_i[d] * O_i[d] per (row, head), in fp32 from the bf16 tensors, stored
-// beside the row's LSE in base 2 (+inf for a row that sees no key, so exp2(x - L2) = 0),
-// head-major: the backward kernels read the pair with one 8-byte load per (row, head), and
-// the stats of a run of rows of one head are contiguous.
-template <int D>
-__global__ __launch_bounds__(256) void delta_kernel(DeltaArgs a) {
-  constexpr int CPH = D / 8;  // 16-byte chunks per head
-  const RowItem it = a.rows[blockIdx.x];
-  const int total = a.hq * CPH;
-  const int64_t base = (int64_t)it.q_row * a.hq * D;
-  for (int e0 = 0; e0 < total; e0 += 256) {
-    const int e = e0 + threadIdx.x;
-    float s = 0.f;
-    if (e < total) {
-      const u32x4_t o = *reinterpret_cast<const u32x4_t*>(a.o + base + (int64_t)e * 8);
-      const u32x4_t g = *reinterpret_cast<const u32x4_t*>(a.dout + base + (int64_t)e * 8);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        s += __uint_as_float(o[w] << 16) * __uint_as_float(g[w] << 16);
-        s += __uint_as_float(o[w] & 0xffff0000u) * __uint_as_float(g[w] & 0xffff0000u);
-      }
-    }
-#pragma unroll
-    for (int off = CPH / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-    if (e < total && (e % CPH) == 0) {
-      const int h = e / CPH;
-      const float L = a.lse[(int64_t)it.q_row * a.hq + h];
-      const float L2 = L == -INFINITY ? INFINITY : L * kLog2e;
-      *reinterpret_cast<f32x2_t*>(a.stats + 2 * ((int64_t)h * a.q_rows + it.q_row)) =
-          f32x2_t{L2, s};
-    }
-  }
-}
-
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream) {
@@ -113,15 +79,6 @@ hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream) {
     hipLaunchKernelGGL((merge_kernel<128>), dim3(a.n_rows), dim3(256), lds, stream, a);
   else
     hipLaunchKernelGGL((merge_kernel<64>), dim3(a.n_rows), dim3(256), lds, stream, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_delta(const DeltaArgs& a, int head_dim, hipStream_t stream) {
-  if (a.n_rows == 0) return hipSuccess;
-  if (head_dim == 128)
-    hipLaunchKernelGGL((delta_kernel<128>), dim3(a.n_rows), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((delta_kernel<64>), dim3(a.n_rows), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

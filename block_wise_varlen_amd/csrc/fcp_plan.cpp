@@ -261,9 +261,6 @@ int make_plan(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t n_pairs, 
     std::vector<QItem> items;
     std::vector<KvSeg> segs;
     group_items(pairs, groups, s, &items, &segs);
-    std::vector<RowItem> rows;
-    for (const Group& g : groups)
-      for (int32_t r = 0; r < g.q_len; ++r) rows.push_back(RowItem{g.q_start + r, r, 0, 0});
     // Elementary KV intervals: cut every KV range at every pair boundary, so each key
     // row belongs to one interval and one dK/dV work item owns it.
     std::vector<int64_t> cuts;
@@ -349,17 +346,15 @@ int make_plan(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t n_pairs, 
                      [](const KvItem& x, const KvItem& y) { return x.cost > y.cost; });
     P.off_qitems = put(&P.blob, items);
     P.off_segs = put(&P.blob, segs);
-    P.off_rows = put(&P.blob, rows);
     P.off_kvitems = put(&P.blob, kvitems);
     P.off_qsegs = put(&P.blob, qsegs);
     P.off_reduce = put(&P.blob, reduce);
     P.n_qitems = (int)items.size();
-    P.n_rows = (int)rows.size();
     P.n_kvitems = (int)kvitems.size();
     P.n_reduce = (int)reduce.size();
     P.n_slots = n_slots;
-    P.off_delta = align_up(P.blob.size());
-    P.off_partial = P.off_delta + align_up((size_t)dims->q_rows * s.hq * 2 * sizeof(float));
+    P.off_stats = align_up(P.blob.size());
+    P.off_partial = P.off_stats + align_up((size_t)dims->q_rows * s.hq * 2 * sizeof(float));
     // Partial slots: dK then dV, each [slot][kv head][kKvTileBwd][D] fp32.
     P.ws_bytes = P.off_partial +
                  align_up(2 * (size_t)n_slots * s.hkv * kKvTileBwd * s.d * sizeof(float));

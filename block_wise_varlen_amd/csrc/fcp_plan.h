@@ -30,7 +30,7 @@ struct Plan {
   std::vector<uint8_t> blob;  // host image of everything uploaded (prefix of ws)
   size_t ws_bytes = 0;        // blob + device-only regions
   size_t off_qitems = 0, off_segs = 0, off_rows = 0, off_parts = 0, off_segout = 0;
-  size_t off_kvitems = 0, off_qsegs = 0, off_delta = 0, off_reduce = 0, off_partial = 0;
+  size_t off_kvitems = 0, off_qsegs = 0, off_stats = 0, off_reduce = 0, off_partial = 0;
   int n_qitems = 0, n_rows = 0, n_kvitems = 0, n_reduce = 0, n_slots = 0;
 };
 

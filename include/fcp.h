@@ -250,7 +250,8 @@ size_t fcp_pipeline_workspace_bytes(const fcp_dims_t* dims, const fcp_stage_t* s
 /*
  * Optional per-kernel timing, for measurement tools (not needed for computing).
  * Kernel ids: FCP_KERNEL_FWD (per-pair forward), FCP_KERNEL_FWD_FUSED, FCP_KERNEL_MERGE,
- * FCP_KERNEL_DELTA (backward preprocessing), FCP_KERNEL_DQ, FCP_KERNEL_DKDV,
+ * FCP_KERNEL_DELTA (reserved: the backward's Delta now runs inside the dQ kernel, so this
+ * id records no launches), FCP_KERNEL_DQ, FCP_KERNEL_DKDV,
  * FCP_KERNEL_DKDV_REDUCE (sums the parts of dK/dV tiles the scheduler split by head),
  * FCP_KERNEL_PIPE_COPY (all copies of one pipeline stage, timed on copy_stream).
  * fcp_timing_enable(1): from now on every kernel launch, from any thread, is bracketed by
