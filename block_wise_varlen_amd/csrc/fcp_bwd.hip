@@ -36,9 +36,11 @@ namespace {
 // dQ kernel
 // ---------------------------------------------------------------------------------
 
-// KV tiles of the dQ kernel go through a ring of this depth (tile t + 3 is issued while
-// tile t is computed).
-constexpr int kDqRing = 4;
+// K/V tiles of the dQ kernel: 128 keys, two LDS slots. The copy of tile t + 2 goes into
+// tile t's slot once every wave has left it (barrier at the end of tile t) and has the
+// whole of tile t + 1's compute to land.
+constexpr int kDqRing = 2;
+constexpr int kDqKt = 128;
 
 template <int D, int CB>
 __global__ __launch_bounds__(64 * kColBlocksPerWG / CB)
@@ -47,8 +49,8 @@ void dq_kernel(BwdArgs a) {
   constexpr int NW = kColBlocksPerWG / CB;  // waves per workgroup
   constexpr int NKC = D / 16;
   constexpr int NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) u16 sK[kDqRing][kKvTile * D];
-  __shared__ __attribute__((aligned(16))) u16 sV[kDqRing][kKvTile * D];
+  __shared__ __attribute__((aligned(16))) u16 sK[kDqRing][kDqKt * D];
+  __shared__ __attribute__((aligned(16))) u16 sV[kDqRing][kDqKt * D];
 
   const int item_idx = blockIdx.x / a.n_hgroups;
   const int hg = blockIdx.x - item_idx * a.n_hgroups;
@@ -115,40 +117,35 @@ void dq_kernel(BwdArgs a) {
 
   const int seg_end = it.seg_begin + it.seg_count;
   const int64_t kv_col = (int64_t)kvh * D;
-  const TileCopy<D, kKvTile, NW> tcopy(kv_stride, wave, lane);
+  const TileCopy<D, kDqKt, NW> tcopy(kv_stride, wave, lane);
   constexpr int NB = kDqRing;
-  constexpr int LOADS = 2 * tile_copy_insts<D, kKvTile, NW>();  // per tile, per wave
-  using Cursor = KvTileCursor<kKvTile>;
+    using Cursor = KvTileCursor<kDqKt>;
   auto advance = [&](const Cursor& x) { return x.next(a.segs, seg_end, it.q_off, it.q_rows); };
   auto copy = [&](const Cursor& x, int b) {
     tcopy(a.k, (int64_t)x.sg.kv_start + x.j0(), x.sg.kv_len - x.j0(), kv_col, sK[b]);
     tcopy(a.v, (int64_t)x.sg.kv_start + x.j0(), x.sg.kv_len - x.j0(), kv_col, sV[b]);
   };
-  // Cursors of the tile being computed and the three after it.
+  // Cursors of the tile being computed and the one after it.
   Cursor cur = Cursor::first(a.segs, it.seg_begin, seg_end, it.q_off, it.q_rows);
-  Cursor n1 = advance(cur), n2 = advance(n1), n3 = advance(n2);
+  Cursor n1 = advance(cur);
   if (cur.valid) copy(cur, 0);
   if (n1.valid) copy(n1, 1);
-  if (n2.valid) copy(n2, 2);
-  // Full wait: the first tiles and this lane's Q / dO registers; it also tells the
+  // Full wait: the first tiles and this lane's Q / dO / O registers; it also tells the
   // compiler that none of its own loads is pending in the loop.
   wait_vmem();
   __syncthreads();
   int buf = 0;
 
   while (cur.valid) {
-    // Every wave has left the slot of tile t - 1 (barrier at the end of the last
-    // iteration), so tile t + 3 may go there.
-    if (n3.valid) copy(n3, buf == 0 ? NB - 1 : buf - 1);
     const KvSeg sg = cur.sg;
     const u16* Kt = sK[buf];
     const u16* Vt = sV[buf];
     const int j0 = cur.j0();
     const bool causal = sg.flags & 1;
-    const bool need_mask = (j0 + kKvTile > sg.kv_len) ||
-                           (causal && j0 + kKvTile - 1 - it.q_off > sg.mask_offset);
+    const bool need_mask = (j0 + kDqKt > sg.kv_len) ||
+                           (causal && j0 + kDqKt - 1 - it.q_off > sg.mask_offset);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < kDqKt / 32; ++kb) {
       f32x16_t S[CB], dP[CB];
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) S[cb] = dP[cb] = zero16();
@@ -212,20 +209,15 @@ void dq_kernel(BwdArgs a) {
       }
     }
 
-    // Tile t + 1 must have landed (t + 2 and t + 3 may stay in flight) before the
-    // barrier that also releases this slot.
-    if (n3.valid)
-      wait_vmem_le<2 * LOADS>();
-    else if (n2.valid)
-      wait_vmem_le<LOADS>();
-    else
-      wait_vmem();
+    // Tile t + 1 (the only copy in flight) must have landed, and every wave must be done
+    // with tile t's slot, before tile t + 2 goes there.
+    const Cursor n2 = advance(n1);
+    if (n1.valid) wait_vmem();
     lds_barrier();
-    buf = buf == NB - 1 ? 0 : buf + 1;
+    if (n2.valid) copy(n2, buf);
+    buf ^= 1;
     cur = n1;
     n1 = n2;
-    n2 = n3;
-    n3 = advance(n3);
   }
 
 #pragma unroll

@@ -11,11 +11,12 @@ namespace fcp {
 
 // Tokens per column block of a forward / dQ tile (one MFMA 32x32 column block).
 constexpr int kColBlock = 32;
-// Column blocks per workgroup: 4 waves x 2 column blocks.
+// Column blocks per forward / dQ workgroup: 8 waves x 1 column block (two waves per SIMD).
 constexpr int kColBlocksPerWG = 8;
-// Keys per KV tile of the forward and dQ kernels.
+// Granularity (keys) of the host's cost estimate that orders forward and dQ work items
+// heaviest first (the kernels themselves stream 128-key tiles).
 constexpr int kKvTile = 64;
-// Keys per workgroup tile of the dK/dV kernel (4 waves x 32 keys).
+// Keys per workgroup tile of the dK/dV kernel (4 SIMD pairs of waves x 32 keys).
 constexpr int kKvTileBwd = 128;
 // Query rows per Q tile streamed by the dK/dV kernel.
 constexpr int kQTileBwd = 32;
