@@ -118,8 +118,8 @@ void dq_kernel(BwdArgs a) {
   const int seg_end = it.seg_begin + it.seg_count;
   const int64_t kv_col = (int64_t)kvh * D;
   const TileCopy<D, kDqKt, NW> tcopy(kv_stride, wave, lane);
-  constexpr int NB = kDqRing;
-    using Cursor = KvTileCursor<kDqKt>;
+  static_assert(kDqRing == 2, "the loop alternates between two slots");
+  using Cursor = KvTileCursor<kDqKt>;
   auto advance = [&](const Cursor& x) { return x.next(a.segs, seg_end, it.q_off, it.q_rows); };
   auto copy = [&](const Cursor& x, int b) {
     tcopy(a.k, (int64_t)x.sg.kv_start + x.j0(), x.sg.kv_len - x.j0(), kv_col, sK[b]);
