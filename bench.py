@@ -256,9 +256,6 @@ def kernel_work(name, wl, pairs):
     if name == "merge":
         parts = int(pairs["q_len"].sum())
         return parts * hq * (4 * d + 4) + q_rows * hq * (2 * d + 4), "byte", "hbm"
-    if name == "bwd_delta":
-        # reads O, dO (bf16) and the LSE; writes (LSE in base 2, Delta)
-        return q_rows * hq * (4 * d + 12), "byte", "hbm"
     if name == "bwd_dkdv_reduce":
         return None, "byte", "hbm"   # depends on the split; never the dominant kernel
     raise KeyError(name)
