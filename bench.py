@@ -218,8 +218,10 @@ class Path:
                                       dq=self.dq, dk=self.dk, dv=self.dv, ws=self.ws)
 
 
-def timed(fn, steps, warmup, kernel_times=False):
-    """Runs fn warmup + steps times; returns (ms per step, per-kernel {name: (ms, n)})."""
+def timed(fn, steps, warmup, kernel_times=False, per_step=None):
+    """Runs fn warmup + steps times; returns (ms per step, per-kernel {name: (ms, n)}).
+    With a list as per_step, also appends each timed step's own duration (events between
+    the steps, inside the same bracketed region)."""
     import torch
     from block_wise_varlen_amd import binding as B
     for _ in range(warmup):
@@ -228,16 +230,18 @@ def timed(fn, steps, warmup, kernel_times=False):
     B.fcp_timing_read()
     if kernel_times:
         B.fcp_timing_enable(True)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
         fn()
-    e1.record()
+        if per_step is not None or i == steps - 1:
+            ev[i + 1].record()
     torch.cuda.synchronize()
     B.fcp_timing_enable(False)
     kt = B.fcp_timing_read()
-    return e0.elapsed_time(e1) / steps, kt
+    if per_step is not None:
+        per_step.extend(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return ev[0].elapsed_time(ev[steps]) / steps, kt
 
 
 def kernel_work(name, wl, pairs):
@@ -459,7 +463,10 @@ def main():
     log("timing fwd+merge")
     ms_f, _ = timed(lambda: path.step(backward=False), args.steps, args.warmup)
     log("timing full step (fwd + merge + bwd)")
-    ms, kt = timed(lambda: path.step(backward=True), args.steps, args.warmup, True)
+    steps_ms = []
+    ms, kt = timed(lambda: path.step(backward=True), args.steps, args.warmup, True,
+                   per_step=steps_ms)
+    steps_ms.sort()
     value = (fl_f + fl_b) / ms / 1e9
     rl = roofline(kt, args.steps, wl, pairs)
     result = {
@@ -477,6 +484,8 @@ def main():
         "fwd_tflops": round(fl_f / ms_f / 1e9, 2),
         "fwd_mfu": round(fl_f / ms_f / 1e9 / PEAK_BF16_TFLOPS, 4),
         "fwd_ms": round(ms_f, 4),
+        "step_ms": {"median": round(steps_ms[len(steps_ms) // 2], 4),
+                    "min": round(steps_ms[0], 4), "max": round(steps_ms[-1], 4)},
         "flops_per_step": fl_f + fl_b,
         "kernel_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in kt.items()},
         "roofline": rl,
