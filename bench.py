@@ -13,7 +13,7 @@ default) adds the 32K single-sequence block-size sweep (512..4096, causal and
 non-causal, forward and forward+backward) as extra fields. Inputs are seeded synthetic
 bf16 N(0,1) data, resident in HBM before timing starts.
 
-Prints one JSON line. ``--gpus`` above 1 is refused: this build runs on one GPU.
+Prints one JSON line. ``--gpus`` above 1 is refused: the library runs on one GPU.
 """
 import argparse
 import json
@@ -420,7 +420,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
     if args.comm_plan:
