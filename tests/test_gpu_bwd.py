@@ -80,13 +80,17 @@ def _key_sample(wl):
     return np.array(sorted(set(rows)), dtype=np.int64)
 
 
-@pytest.mark.parametrize("cfg", ["config2", "config3-1024", "config3-4096-nc"])
+@pytest.mark.parametrize("cfg", ["config2", "config2-s1", "config2-s2", "config3-1024",
+                                 "config3-4096-nc"])
 def test_full_size_sampled(gpu, cfg):
     import torch
+    seed = {"config2-s1": 1, "config2-s2": 2}.get(cfg, 0)
     wl = {"config2": lambda: W.config2(0),
+          "config2-s1": lambda: W.config2(1),
+          "config2-s2": lambda: W.config2(2),
           "config3-1024": lambda: W.config3(1024, True),
           "config3-4096-nc": lambda: W.config3(4096, False)}[cfg]()
-    dev, x = U.inputs(wl, seed=0)
+    dev, x = U.inputs(wl, seed=seed)
     pairs = build_pairs(wl)
     _, _, dq, dk, dv = _fwd_bwd(wl, dev, pairs)
     torch.cuda.synchronize()

@@ -92,15 +92,21 @@ def test_forward_is_deterministic(gpu):
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-@pytest.mark.parametrize("cfg", ["config2", "config3-512", "config3-4096", "config3-1024-nc"])
+@pytest.mark.parametrize("cfg", ["config2", "config2-s1", "config2-s2", "config3-512",
+                                 "config3-4096", "config3-1024-nc"])
 def test_full_size_sampled(gpu, cfg):
-    """The bench's launch configuration at full size, checked on sampled rows."""
+    """The bench's launch configuration at full size, checked on sampled rows. The 1K
+    worker share also runs at seeds 1 and 2, which draw other length mixes (6201/10183
+    and 5139/2187/2495/6563 tokens) and other tensor values."""
     import torch
+    seed = {"config2-s1": 1, "config2-s2": 2}.get(cfg, 0)
     wl = {"config2": lambda: W.config2(0),
+          "config2-s1": lambda: W.config2(1),
+          "config2-s2": lambda: W.config2(2),
           "config3-512": lambda: W.config3(512, True),
           "config3-4096": lambda: W.config3(4096, True),
           "config3-1024-nc": lambda: W.config3(1024, False)}[cfg]()
-    dev, x = U.inputs(wl, seed=0, which=("q", "k", "v"))
+    dev, x = U.inputs(wl, seed=seed, which=("q", "k", "v"))
     pairs = build_pairs(wl)
     o_part, lse_part = _run_partials(wl, dev, pairs)
     o, lse = B.fcp_merge_partials(pairs, o_part, lse_part, wl.q_rows, wl.num_kv_heads)
