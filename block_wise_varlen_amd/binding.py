@@ -134,9 +134,11 @@ def _need(t, dtype, name):
         raise TypeError("%s must be a contiguous %s CUDA tensor" % (name, dtype))
 
 
-def _workspace(size_fn, like, ws):
+def _workspace(size_fn, like, ws, stream=None):
     """The caller's workspace as given (the library checks its size), or a new one of
-    size_fn() bytes."""
+    size_fn() bytes. A new one is freed when the wrapper returns, while the call may
+    still be reading it on ``stream``: it is recorded on that stream, so torch's caching
+    allocator hands its memory out again only once the stream has passed the call."""
     import torch
     if ws is not None:
         return ws, ws.numel() * ws.element_size()
@@ -144,6 +146,8 @@ def _workspace(size_fn, like, ws):
     if nbytes == 0:
         return None, 0
     ws = torch.empty(nbytes, dtype=torch.uint8, device=like.device)
+    if stream is not None:
+        ws.record_stream(stream)
     return ws, nbytes
 
 
@@ -193,7 +197,7 @@ def fcp_block_attn_fwd(q, k, v, pairs, o_part=None, lse_part=None, part_rows=Non
     dims = _dims_from(q, k, part_rows, softmax_scale)
     lib = load()
     ws, wsb = _workspace(lambda: lib.fcp_workspace_bytes(ctypes.byref(dims), p, n, FCP_OP_FWD),
-                         q, ws)
+                         q, ws, stream)
     _check(lib.fcp_block_attn_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), p, n,
                                   _ptr(o_part), _ptr(lse_part), _ptr(ws), wsb,
                                   _stream(q, stream)))
@@ -218,7 +222,8 @@ def fcp_merge_partials(pairs, o_part, lse_part, q_rows, num_kv_heads=1, o=None, 
     dims = make_dims(hq, num_kv_heads, d, q_rows, 0, o_part.shape[0])
     lib = load()
     ws, wsb = _workspace(
-        lambda: lib.fcp_workspace_bytes(ctypes.byref(dims), p, n, FCP_OP_MERGE), o_part, ws)
+        lambda: lib.fcp_workspace_bytes(ctypes.byref(dims), p, n, FCP_OP_MERGE), o_part, ws,
+        stream)
     _check(lib.fcp_merge_partials(ctypes.byref(dims), p, n, _ptr(o_part), _ptr(lse_part),
                                   _ptr(o), _ptr(lse), _ptr(ws), wsb, _stream(o_part, stream)))
     return o, lse
@@ -240,7 +245,8 @@ def fcp_block_attn_fwd_fused(q, k, v, pairs, o=None, lse=None, softmax_scale=0.0
     dims = _dims_from(q, k, 0, softmax_scale)
     lib = load()
     ws, wsb = _workspace(
-        lambda: lib.fcp_workspace_bytes(ctypes.byref(dims), p, n, FCP_OP_FWD_FUSED), q, ws)
+        lambda: lib.fcp_workspace_bytes(ctypes.byref(dims), p, n, FCP_OP_FWD_FUSED), q, ws,
+        stream)
     _check(lib.fcp_block_attn_fwd_fused(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), p, n,
                                         _ptr(o), _ptr(lse), _ptr(ws), wsb, _stream(q, stream)))
     return o, lse
@@ -265,7 +271,7 @@ def fcp_block_attn_bwd(q, k, v, o, lse, dout, pairs, dq=None, dk=None, dv=None,
     dims = _dims_from(q, k, 0, softmax_scale)
     lib = load()
     ws, wsb = _workspace(lambda: lib.fcp_workspace_bytes(ctypes.byref(dims), p, n, FCP_OP_BWD),
-                         q, ws)
+                         q, ws, stream)
     _check(lib.fcp_block_attn_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                   _ptr(lse), _ptr(dout), p, n, _ptr(dq), _ptr(dk), _ptr(dv),
                                   _ptr(ws), wsb, _stream(q, stream)))
@@ -313,7 +319,7 @@ def fcp_pipeline_fwd(q, k, v, k_src, v_src, stages, copies, pairs, o_part, lse_p
     src_rows = k_src.shape[0]
     ws, wsb = _workspace(lambda: lib.fcp_pipeline_workspace_bytes(ctypes.byref(dims), sp, ns,
                                                                   cpp, pp, int(depth), src_rows),
-                         q, ws)
+                         q, ws, stream)
     s = _stream(q, stream)
     cs = s if copy_stream is None else ctypes.c_void_p(copy_stream.cuda_stream)
     _check(lib.fcp_pipeline_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(k_src),
