@@ -22,7 +22,8 @@ FCP_OP_FWD, FCP_OP_MERGE, FCP_OP_BWD, FCP_OP_FWD_FUSED = range(4)
 # Every symbol include/fcp.h declares.
 SYMBOLS = ("fcp_abi_version", "fcp_status_string", "fcp_last_error", "fcp_validate",
            "fcp_workspace_bytes", "fcp_block_attn_fwd", "fcp_merge_partials",
-           "fcp_block_attn_fwd_fused", "fcp_block_attn_bwd", "fcp_timing_enable",
+           "fcp_block_attn_fwd_fused", "fcp_block_attn_fwd_fused_noalloc",
+           "fcp_block_attn_bwd", "fcp_timing_enable",
            "fcp_timing_read", "fcp_kernel_name", "fcp_comm_plan", "fcp_pipeline_fwd",
            "fcp_pipeline_workspace_bytes")
 FCP_KERNEL_COUNT = 8
@@ -72,6 +73,7 @@ def load():
         "fcp_block_attn_fwd": (ctypes.c_int, [D, P, P, P, P, I32, P, P, P, SZ, P]),
         "fcp_merge_partials": (ctypes.c_int, [D, P, I32, P, P, P, P, P, SZ, P]),
         "fcp_block_attn_fwd_fused": (ctypes.c_int, [D, P, P, P, P, I32, P, P, P, SZ, P]),
+        "fcp_block_attn_fwd_fused_noalloc": (ctypes.c_int, [D, P, P, P, P, I32, P, P, P]),
         "fcp_block_attn_bwd": (ctypes.c_int, [D, P, P, P, P, P, P, P, I32, P, P, P, P, SZ,
                                               P]),
         "fcp_timing_enable": (ctypes.c_int, [ctypes.c_int]),
@@ -249,6 +251,28 @@ def fcp_block_attn_fwd_fused(q, k, v, pairs, o=None, lse=None, softmax_scale=0.0
         stream)
     _check(lib.fcp_block_attn_fwd_fused(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), p, n,
                                         _ptr(o), _ptr(lse), _ptr(ws), wsb, _stream(q, stream)))
+    return o, lse
+
+
+def fcp_block_attn_fwd_fused_noalloc(q, k, v, pairs, o=None, lse=None, softmax_scale=0.0,
+                                     stream=None):
+    """fcp_block_attn_fwd_fused with its work lists in the library's static device array
+    (no workspace argument; the library allocates nothing). Outputs are allocated here
+    only when not given."""
+    import torch
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, nm)
+    if o is None:
+        o = torch.zeros_like(q)
+    if lse is None:
+        lse = torch.zeros((q.shape[0], q.shape[1]), dtype=torch.float32, device=q.device)
+    _need(o, torch.bfloat16, "o")
+    _need(lse, torch.float32, "lse")
+    arr, p, n = _pairs_arg(pairs)
+    dims = _dims_from(q, k, 0, softmax_scale)
+    _check(load().fcp_block_attn_fwd_fused_noalloc(ctypes.byref(dims), _ptr(q), _ptr(k),
+                                                   _ptr(v), p, n, _ptr(o), _ptr(lse),
+                                                   _stream(q, stream)))
     return o, lse
 
 

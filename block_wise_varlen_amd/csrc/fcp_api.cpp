@@ -206,6 +206,33 @@ const T* at(void* ws, size_t off) {
   return reinterpret_cast<const T*>(static_cast<char*>(ws) + off);
 }
 
+// Work lists of fcp_block_attn_fwd_fused_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends. Host code never uses the array's name as an
+// address (on the host it is only a stand-in for the symbol): each device's address of
+// its copy is looked up once, with that device current, and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_err(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return set_err(FCP_ERR_UNSUPPORTED, "device id above 63");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_err(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return set_err(FCP_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FCP_OK;
+}
+
 template <class F>
 int guarded(F&& f) {
   try {
@@ -355,6 +382,50 @@ int fcp_block_attn_fwd_fused(const fcp_dims_t* dims, const void* q, const void* 
     const hipError_t e = timed(FCP_KERNEL_FWD_FUSED, stream,
                                 [&] { return fcp::launch_fwd(a, s.d, true, stream); });
     return e == hipSuccess ? FCP_OK : hip_err(e, "fused forward launch");
+  });
+}
+
+int fcp_block_attn_fwd_fused_noalloc(const fcp_dims_t* dims, const void* q, const void* k,
+                                     const void* v, const fcp_pair_t* pairs, int32_t n_pairs,
+                                     void* o, float* lse, hipStream_t stream) {
+  return guarded([&] {
+    fcp::Plan P;
+    std::string msg;
+    int st = fcp::make_plan(dims, pairs, n_pairs, FCP_OP_FWD_FUSED, &P, &msg);
+    if (st != FCP_OK) return set_err(st, msg);
+    if (n_pairs == 0) return FCP_OK;
+    st = need_ptrs({q, k, v, o, lse});
+    if (st != FCP_OK) return st;
+    // Checked before any HIP call: an oversized table never reaches the device.
+    if (P.ws_bytes > kScratchBytes)
+      return set_err(FCP_ERR_WORKSPACE,
+                     "work lists need " + std::to_string(P.ws_bytes) +
+                         " bytes, above the " + std::to_string(kScratchBytes) +
+                         "-byte static scratch of fcp_block_attn_fwd_fused_noalloc; use "
+                         "fcp_block_attn_fwd_fused with a workspace");
+    st = check_device();
+    if (st != FCP_OK) return st;
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != FCP_OK) return st;
+    // From pageable host memory: the runtime has taken the bytes when the call returns,
+    // and the copy is ordered on `stream` after earlier work that reads the array.
+    hipError_t e = hipMemcpyAsync(ws, P.blob.data(), P.blob.size(), hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_err(e, "work-list upload (static scratch)");
+    const fcp::Shape& s = P.shape;
+    fcp::FwdArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.items = at<fcp::QItem>(ws, P.off_qitems);
+    a.segs = at<fcp::KvSeg>(ws, P.off_segs);
+    a.n_items = P.n_qitems;
+    a.hq = s.hq, a.hkv = s.hkv, a.group = s.group, a.hpw = s.hpw, a.n_hgroups = s.n_hgroups;
+    a.scale_log2 = s.scale * 1.4426950408889634f;
+    a.o = static_cast<uint16_t*>(o);
+    a.lse = lse;
+    e = fcp::launch_fwd(a, s.d, true, stream);
+    return e == hipSuccess ? FCP_OK : hip_err(e, "fused forward launch (static scratch)");
   });
 }
 

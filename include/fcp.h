@@ -32,7 +32,8 @@
  *  - `ws` is caller-owned device scratch of at least fcp_workspace_bytes(...) bytes for
  *    the same op and arguments; it must stay untouched until the stream passes the
  *    call. The library allocates no device memory; it owns only pinned host staging
- *    buffers used to upload its work lists, reused once their copies complete.
+ *    buffers used to upload its work lists, reused once their copies complete, and
+ *    the 4 MiB static device array of fcp_block_attn_fwd_fused_noalloc.
  *  - Calls enqueue work on `stream` and return without waiting for it. They may be
  *    issued concurrently from several threads on distinct streams. Calls that share a
  *    workspace or output buffers must be ordered by the caller.
@@ -177,6 +178,25 @@ int fcp_block_attn_fwd_fused(const fcp_dims_t* dims, const void* q, const void* 
                              const void* v, const fcp_pair_t* pairs, int32_t n_pairs,
                              void* o, float* lse, void* ws, size_t ws_bytes,
                              hipStream_t stream);
+
+/*
+ * For callers that cannot allocate memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): fcp_block_attn_fwd_fused without a workspace
+ * argument. Same arguments, checks and results as fcp_block_attn_fwd_fused (bitwise:
+ * same kernel, same work lists); the work lists go to a static device array of 4 MiB
+ * that the library holds on each GPU it runs on until the process ends, instead of `ws`.
+ * The call allocates no device or pinned memory (the host planner uses ordinary heap
+ * memory) and uploads the lists from pageable host memory with one hipMemcpyAsync on
+ * `stream`. Tables whose work lists exceed 4 MiB (about 130 000 tiles of 32 query rows,
+ * i.e. some 4 million query rows at 8 heads per KV head) return FCP_ERR_WORKSPACE before
+ * any HIP call. Every call on one GPU shares that GPU's array, which keeps the last
+ * call's lists: calls on one stream are ordered, but calls that overlap on one GPU
+ * (different streams or threads without ordering) race on the array and must not be
+ * issued.
+ */
+int fcp_block_attn_fwd_fused_noalloc(const fcp_dims_t* dims, const void* q, const void* k,
+                                     const void* v, const fcp_pair_t* pairs, int32_t n_pairs,
+                                     void* o, float* lse, hipStream_t stream);
 
 /*
  * Backward (FCP paper Sec. 2.2 states that a backward is implemented; the gradient

@@ -1,6 +1,7 @@
 """The C ABI library on the host: it loads, exports every symbol include/fcp.h
 declares, and its host-only calls (validation, workspace sizing, status text) behave.
-No compute entry point is called here."""
+A compute entry point is called here only with arguments it rejects before any HIP
+call."""
 import ctypes
 import os
 import re
@@ -135,3 +136,25 @@ def test_workloads_validate(lib, cfg):
     for op in (B.FCP_OP_FWD, B.FCP_OP_MERGE, B.FCP_OP_BWD, B.FCP_OP_FWD_FUSED):
         assert B.fcp_validate(dims, pairs, op) == B.FCP_OK, B.fcp_last_error()
         assert B.fcp_workspace_bytes(dims, pairs, op) > 0
+
+
+def test_noalloc_rejects_tables_beyond_its_static_scratch(lib):
+    """fcp_block_attn_fwd_fused_noalloc keeps its work lists in a 4 MiB static device
+    array: a table needing more (5e6 query rows -> 156 250 tiles of 32 rows, 5 MB of
+    32-byte items) is refused with FCP_ERR_WORKSPACE before any HIP call, so fake
+    (never dereferenced) tensor pointers serve here."""
+    rows = 5_000_000
+    dims = B.make_dims(8, 1, 64, rows, rows)
+    pairs = _pairs([(0, 0, rows, 0, 1, 0, 0, 0)])
+    assert B.fcp_validate(dims, pairs, B.FCP_OP_FWD_FUSED) == B.FCP_OK
+    assert B.fcp_workspace_bytes(dims, pairs, B.FCP_OP_FWD_FUSED) > (4 << 20)
+    fake = ctypes.c_void_p(1 << 20)
+    arr = np.ascontiguousarray(pairs)
+    st = lib.fcp_block_attn_fwd_fused_noalloc(ctypes.byref(dims), fake, fake, fake,
+                                              arr.ctypes.data_as(ctypes.c_void_p), 1, fake,
+                                              fake, None)
+    assert st == B.FCP_ERR_WORKSPACE
+    assert "static scratch" in B.fcp_last_error()
+    # n_pairs == 0 is a no-op even with NULL tensors
+    assert lib.fcp_block_attn_fwd_fused_noalloc(ctypes.byref(dims), None, None, None, None, 0,
+                                                None, None, None) == B.FCP_OK
