@@ -25,7 +25,7 @@ SYMBOLS = ("fcp_abi_version", "fcp_status_string", "fcp_last_error", "fcp_valida
            "fcp_block_attn_fwd_fused", "fcp_block_attn_fwd_fused_noalloc",
            "fcp_block_attn_bwd", "fcp_timing_enable",
            "fcp_timing_read", "fcp_kernel_name", "fcp_comm_plan", "fcp_pipeline_fwd",
-           "fcp_pipeline_workspace_bytes")
+           "fcp_pipeline_workspace_bytes", "fcp_plan_info")
 FCP_KERNEL_COUNT = 8
 FCP_PIPE_COPY_SHADER = 1
 
@@ -83,6 +83,7 @@ def load():
         "fcp_pipeline_fwd": (ctypes.c_int, [D, P, P, P, P, P, ctypes.c_int64, P, I32, P, P,
                                             I32, P, P, P, P, I32, P, SZ, P, P]),
         "fcp_pipeline_workspace_bytes": (SZ, [D, P, I32, P, P, I32, ctypes.c_int64]),
+        "fcp_plan_info": (ctypes.c_int, [D, P, I32, ctypes.c_int, P, I32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -178,6 +179,18 @@ def fcp_workspace_bytes(dims, pairs, op):
 
 
 # ---- device entry points ----------------------------------------------------------
+
+PLAN_INFO_FIELDS = ("qitems", "kvitems", "split_tiles", "slots", "multihead_parts",
+                    "multihead_offset_parts", "ws_bytes")
+
+
+def fcp_plan_info(dims, pairs, op):
+    """{field: int} summary of the work lists ``op`` builds (host only)."""
+    arr, p, n = _pairs_arg(pairs)
+    out = (ctypes.c_int64 * len(PLAN_INFO_FIELDS))()
+    _check(load().fcp_plan_info(ctypes.byref(dims), p, n, op, out, len(PLAN_INFO_FIELDS)))
+    return dict(zip(PLAN_INFO_FIELDS, (int(x) for x in out)))
+
 
 def fcp_block_attn_fwd(q, k, v, pairs, o_part=None, lse_part=None, part_rows=None,
                        softmax_scale=0.0, ws=None, stream=None):

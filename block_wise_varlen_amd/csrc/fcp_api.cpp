@@ -318,6 +318,34 @@ int fcp_validate(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t n_pair
   });
 }
 
+int fcp_plan_info(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t n_pairs, int op,
+                  int64_t* out, int32_t n_out) {
+  return guarded([&] {
+    if (n_out < 0 || (n_out > 0 && !out)) return set_err(FCP_ERR_INVALID_ARG, "bad output array");
+    fcp::Plan P;
+    std::string msg;
+    const int st = fcp::make_plan(dims, pairs, n_pairs, op, &P, &msg);
+    if (st != FCP_OK) return set_err(st, msg);
+    int64_t v[FCP_PLAN_INFO_COUNT] = {};
+    v[FCP_PLAN_QITEMS] = P.n_qitems;
+    v[FCP_PLAN_KVITEMS] = P.n_kvitems;
+    v[FCP_PLAN_SPLIT_TILES] = P.n_reduce;
+    v[FCP_PLAN_SLOTS] = P.n_slots;
+    v[FCP_PLAN_WS_BYTES] = (int64_t)P.ws_bytes;
+    if (P.n_kvitems > 0) {
+      const fcp::KvItem* it = reinterpret_cast<const fcp::KvItem*>(P.blob.data() + P.off_kvitems);
+      for (int i = 0; i < P.n_kvitems; ++i) {
+        if (it[i].slot < 0) continue;
+        const int first = it[i].heads & 0xffff, count = it[i].heads >> 16;
+        if (count > 1) ++v[FCP_PLAN_MULTIHEAD_PARTS];
+        if (count > 1 && first > 0) ++v[FCP_PLAN_MULTIHEAD_OFFSET_PARTS];
+      }
+    }
+    for (int32_t i = 0; i < n_out; ++i) out[i] = i < FCP_PLAN_INFO_COUNT ? v[i] : 0;
+    return FCP_OK;
+  });
+}
+
 size_t fcp_workspace_bytes(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t n_pairs,
                            int op) {
   size_t out = 0;

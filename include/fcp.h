@@ -144,6 +144,33 @@ size_t fcp_workspace_bytes(const fcp_dims_t* dims, const fcp_pair_t* pairs,
                            int32_t n_pairs, int op);
 
 /*
+ * Host-only summary of the work lists that `op` builds for these dims and pairs (the
+ * varlen tile scheduler's output; no HIP call), for tests and tools. Writes n_out int64
+ * values to `out` (entries past FCP_PLAN_INFO_COUNT are 0):
+ *   FCP_PLAN_QITEMS                  forward / dQ work items (Q tiles; each runs on
+ *                                    num_q_heads / min(G, 8) workgroups)
+ *   FCP_PLAN_KVITEMS                 dK/dV work items (BWD), after head splitting
+ *   FCP_PLAN_SPLIT_TILES             dK/dV key tiles split by query heads (BWD)
+ *   FCP_PLAN_SLOTS                   partial dK/dV slots of the split tiles (BWD)
+ *   FCP_PLAN_MULTIHEAD_PARTS         parts of split tiles holding more than one head
+ *   FCP_PLAN_MULTIHEAD_OFFSET_PARTS  of those, parts whose first head is not the first
+ *                                    of the group
+ *   FCP_PLAN_WS_BYTES                fcp_workspace_bytes() for the same arguments
+ * Returns the status fcp_validate would return, or FCP_ERR_INVALID_ARG for a bad `out`.
+ */
+#define FCP_PLAN_QITEMS 0
+#define FCP_PLAN_KVITEMS 1
+#define FCP_PLAN_SPLIT_TILES 2
+#define FCP_PLAN_SLOTS 3
+#define FCP_PLAN_MULTIHEAD_PARTS 4
+#define FCP_PLAN_MULTIHEAD_OFFSET_PARTS 5
+#define FCP_PLAN_WS_BYTES 6
+#define FCP_PLAN_INFO_COUNT 7
+
+int fcp_plan_info(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t n_pairs, int op,
+                  int64_t* out, int32_t n_out);
+
+/*
  * Forward, one partial per pair (FCP paper Sec. 2.2: per-slice intermediate results).
  * For every pair and query head, writes the pair's own normalised attention output
  * over its visible keys to o_part rows [out_row, out_row + q_len) and its natural-log

@@ -263,3 +263,56 @@ def dkv_rows(qf, kf, vf, dof, idx, kv_rows, scale=None):
                 dk[ki, g] += (ds @ qf[rc, h]) * sc
                 dv[ki, g] += p @ dout
     return dk, dv
+
+
+def dkv_keys(qf, kf, vf, dof, idx, kv_rows, heads=None, scale=None):
+    """dK and dV at the given KV rows, from the query heads in ``heads`` (all by default):
+    for every sequence holding one of the rows, each owned query of that sequence is run
+    forward once (its LSE, O and Delta over all of its visible keys), and only the
+    requested keys' columns of P and dS are kept. A KV head's rows are exact when
+    ``heads`` holds its whole query-head group (or when dO is zero on the other heads of
+    the group). Returns (dK, dV), each [len(kv_rows), Hkv, D]."""
+    kv_rows = np.asarray(kv_rows, dtype=np.int64)
+    heads = list(range(idx.hq)) if heads is None else list(heads)
+    group = idx.hq // idx.hkv
+    sc = _scale(idx.d, scale)
+    dk = np.zeros((len(kv_rows), idx.hkv, idx.d))
+    dv = np.zeros((len(kv_rows), idx.hkv, idx.d))
+    where = {}
+    for s, m in idx.kv_row_of_pos.items():
+        for p in np.nonzero(np.isin(m, kv_rows))[0]:
+            for ki in np.nonzero(kv_rows == m[p])[0]:
+                where.setdefault(s, []).append((int(ki), int(p)))
+    rows = idx.owned_rows()
+    for s, sel in where.items():
+        kis = np.array([a for a, _ in sel])
+        kps = np.array([b for _, b in sel])
+        r = rows[idx.q_row_seq[rows] == s]
+        if len(r) == 0:
+            continue
+        pos = idx.q_row_pos[r]
+        krows = idx.visible_key_rows(s, pos.max())
+        kpos = np.arange(len(krows))
+        step = _chunk(len(krows))
+        for a in range(0, len(r), step):
+            rc, qp = r[a:a + step], pos[a:a + step]
+            mask = (kpos[None, :] <= qp[:, None]) if idx.causal else None
+            for h in heads:
+                g = h // group
+                kk, vv = kf[krows, g], vf[krows, g]
+                smat = (qf[rc, h] @ kk.T) * sc
+                if mask is not None:
+                    smat = np.where(mask, smat, -np.inf)
+                m = smat.max(axis=1, keepdims=True)
+                lse = m[:, 0] + np.log(np.exp(smat - m).sum(axis=1))
+                p = np.exp(smat - lse[:, None])
+                dout = dof[rc, h]
+                delta = (dout * (p @ vv)).sum(axis=1)
+                # columns of the requested keys (keys past a query's position have P = 0)
+                inside = kps < len(krows)
+                cols = np.where(inside, kps, 0)
+                psel = np.where(inside[None, :], p[:, cols], 0.0)
+                ds = psel * (dout @ vv[cols].T - delta[:, None])
+                dk[kis, g] += (ds.T @ qf[rc, h]) * sc
+                dv[kis, g] += psel.T @ dout
+    return dk, dv

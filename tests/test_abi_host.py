@@ -158,3 +158,28 @@ def test_noalloc_rejects_tables_beyond_its_static_scratch(lib):
     # n_pairs == 0 is a no-op even with NULL tensors
     assert lib.fcp_block_attn_fwd_fused_noalloc(ctypes.byref(dims), None, None, None, None, 0,
                                                 None, None, None) == B.FCP_OK
+
+
+def test_plan_info(lib):
+    """The scheduler summary: config 2's heaviest key tiles split into two parts of four
+    query heads (the second starting at head 4); a 32K single sequence splits nothing."""
+    wl = W.config2(0)
+    pairs = build_pairs(wl)
+    dims = B.make_dims(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.q_rows, wl.kv_rows)
+    info = B.fcp_plan_info(dims, pairs, B.FCP_OP_BWD)
+    assert info["split_tiles"] > 0 and info["slots"] == 2 * info["split_tiles"]
+    assert info["multihead_parts"] == info["slots"]
+    assert info["multihead_offset_parts"] == info["split_tiles"]
+    assert info["ws_bytes"] == B.fcp_workspace_bytes(dims, pairs, B.FCP_OP_BWD)
+    fwd = B.fcp_plan_info(dims, pairs, B.FCP_OP_FWD_FUSED)
+    # one work item per 32-row tile of each distinct Q range (a Q segment here)
+    assert fwd["kvitems"] == 0
+    assert fwd["qitems"] == sum(-(-s.length // 32) for s in wl.q_segments())
+    wl = W.config3(1024, True)
+    pairs = build_pairs(wl)
+    dims = B.make_dims(64, 8, 128, wl.q_rows, wl.kv_rows)
+    info = B.fcp_plan_info(dims, pairs, B.FCP_OP_BWD)
+    assert info["split_tiles"] == 0 and info["kvitems"] == 256
+    bad = B.make_dims(64, 7, 128, 10, 10)
+    with pytest.raises(B.FcpError):
+        B.fcp_plan_info(bad, pairs, B.FCP_OP_BWD)

@@ -80,16 +80,13 @@ def _key_sample(wl):
     return np.array(sorted(set(rows)), dtype=np.int64)
 
 
-@pytest.mark.parametrize("cfg", ["config2", "config2-s1", "config2-s2", "config3-1024",
-                                 "config3-4096-nc"])
+@pytest.mark.parametrize("cfg", ["config2", "config2-s1", "config2-s2"])
 def test_full_size_sampled(gpu, cfg):
     import torch
     seed = {"config2-s1": 1, "config2-s2": 2}.get(cfg, 0)
     wl = {"config2": lambda: W.config2(0),
           "config2-s1": lambda: W.config2(1),
-          "config2-s2": lambda: W.config2(2),
-          "config3-1024": lambda: W.config3(1024, True),
-          "config3-4096-nc": lambda: W.config3(4096, False)}[cfg]()
+          "config2-s2": lambda: W.config2(2)}[cfg]()
     dev, x = U.inputs(wl, seed=seed)
     pairs = build_pairs(wl)
     _, _, dq, dk, dv = _fwd_bwd(wl, dev, pairs)
@@ -160,3 +157,145 @@ def test_full_size_heterogeneous(gpu):
             .sum(dim=(0, 2))
         rel = (torch.linalg.norm(lhs - rhs) / torch.linalg.norm(rhs)).item()
         assert rel < 2e-2, (s, rel)
+
+
+def _plan(wl, pairs):
+    dims = B.make_dims(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.q_rows, wl.kv_rows)
+    return B.fcp_plan_info(dims, pairs, B.FCP_OP_BWD)
+
+
+def _seq_rows(wl, idx, s):
+    qrows = np.nonzero(idx.q_row_seq == s)[0]
+    krows = np.asarray(idx.kv_row_of_pos[s])
+    return qrows, krows[krows >= 0]
+
+
+def test_whole_sequence_with_head_split_tiles(gpu):
+    """The 1K worker share at full size (seed 0: sequences of 4763, 3496 and 8125
+    tokens): every dQ row and every dK/dV key of the 8125-token sequence, element-wise
+    against the oracle's full backward of that sequence. Its first key tiles are seen by
+    so many query tiles that the scheduler splits them into two parts of four query
+    heads each (the second starting at head 4), summed by the reduce kernel."""
+    import torch
+    wl = W.config2(0)
+    dev, x = U.inputs(wl, seed=0)
+    pairs = build_pairs(wl)
+    info = _plan(wl, pairs)
+    assert info["split_tiles"] > 0 and info["multihead_offset_parts"] > 0, info
+    _, _, dq, dk, dv = _fwd_bwd(wl, dev, pairs)
+    torch.cuda.synchronize()
+    idx = oracle.SeqIndex(wl)
+    s = int(np.argmax(wl.seqlens))
+    rq, rk, rv = oracle.backward(x["q"], x["k"], x["v"], x["do"], idx, seqs=[s])
+    qrows, krows = _seq_rows(wl, idx, s)
+    check_grad(dq.cpu().numpy()[qrows], rq[qrows], "seq %d dQ" % s)
+    check_grad(dk.cpu().numpy()[krows], rk[krows], "seq %d dK" % s)
+    check_grad(dv.cpu().numpy()[krows], rv[krows], "seq %d dV" % s)
+
+
+def test_multihead_parts_mid_size(gpu):
+    """A mid-size share (3000, 1100 and 2900 tokens in 1K blocks, 64/8 heads, D 128) whose
+    heavy key tiles the scheduler splits into 2 to 4 parts of 2 or 3 query heads, most of
+    them starting past the group's first head: all of dQ, dK and dV element-wise."""
+    import torch
+    wl = W.custom([3000, 1100, 2900], 1024, 64, 8, 128, True)
+    dev, x = U.inputs(wl, seed=8)
+    pairs = build_pairs(wl)
+    info = _plan(wl, pairs)
+    assert info["multihead_parts"] > 0 and info["multihead_offset_parts"] > 0, info
+    assert info["slots"] < 8 * info["split_tiles"], info   # not one head per part
+    _, _, dq, dk, dv = _fwd_bwd(wl, dev, pairs)
+    torch.cuda.synchronize()
+    idx = oracle.SeqIndex(wl)
+    rq, rk, rv = oracle.backward(x["q"], x["k"], x["v"], x["do"], idx)
+    rows = idx.owned_rows()
+    check_grad(dq.cpu().numpy()[rows], rq[rows], "mid dQ")
+    check_grad(dk.cpu().numpy(), rk, "mid dK")
+    check_grad(dv.cpu().numpy(), rv, "mid dV")
+
+
+def _one_head(do, h0):
+    import torch
+    out = torch.zeros_like(do)
+    out[:, h0] = do[:, h0]
+    return out
+
+
+def test_heterogeneous_dk_dv(gpu):
+    """The heaviest worker of the heterogeneous batch: dK and dV element-wise on every
+    key of each of its fully owned short packed sequences (all query heads); then, with
+    the upstream gradient kept on one query head, at early keys (seen by every owned
+    query) and late keys of a 15K-token and a 262K-token sequence whose KV blocks were
+    pulled."""
+    import torch
+    wl = W.config5(0)
+    dev = W.make_device_inputs(wl, seed=0)
+    pairs = build_pairs(wl)
+    o, lse = B.fcp_block_attn_fwd_fused(dev["q"], dev["k"], dev["v"], pairs)
+    _, dk, dv = B.fcp_block_attn_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], pairs)
+    torch.cuda.synchronize()
+    idx = oracle.SeqIndex(wl)
+    xr = {n: U.DeviceRows(dev[n]) for n in ("q", "k", "v", "do")}
+    rows = idx.owned_rows()
+    seqs, counts = np.unique(idx.q_row_seq[rows], return_counts=True)
+    short = [int(s) for s, c in zip(seqs, counts) if c == wl.seqlens[s] and c <= 4096]
+    assert len(short) >= 3, short
+    keys = np.concatenate([_seq_rows(wl, idx, s)[1] for s in short])
+    rk, rv = oracle.dkv_keys(xr["q"], xr["k"], xr["v"], xr["do"], idx, keys)
+    kidx = torch.as_tensor(keys, device=dk.device)
+    check_grad(dk.index_select(0, kidx).cpu().numpy(), rk, "config5 short seqs dK")
+    check_grad(dv.index_select(0, kidx).cpu().numpy(), rv, "config5 short seqs dV")
+    del dk, dv
+
+    h0 = 29
+    g0 = h0 // (wl.num_q_heads // wl.num_kv_heads)
+    _, dk1, dv1 = B.fcp_block_attn_bwd(dev["q"], dev["k"], dev["v"], o, lse,
+                                       _one_head(dev["do"], h0), pairs)
+    torch.cuda.synchronize()
+    picks = []
+    for length in (15189, 262094):
+        s = wl.seqlens.index(length)
+        qrows, krows = _seq_rows(wl, idx, s)
+        assert len(qrows) > 0 and len(krows) > 0
+        p0, p1 = int(idx.q_row_pos[qrows].min()), int(idx.q_row_pos[qrows].max())
+        for p in (0, 1, 127, 128, 4095, p0 - 1, p0, p0 + 100, p1):
+            picks.append(int(idx.kv_row_of_pos[s][p]))
+    keys = np.array(sorted(set(picks)))
+    rk, rv = oracle.dkv_keys(xr["q"], xr["k"], xr["v"], xr["do"], idx, keys, heads=[h0])
+    kidx = torch.as_tensor(keys, device=dk1.device)
+    check_grad(dk1.index_select(0, kidx)[:, g0].cpu().numpy(), rk[:, g0], "config5 dK keys")
+    check_grad(dv1.index_select(0, kidx)[:, g0].cpu().numpy(), rv[:, g0], "config5 dV keys")
+
+
+def test_zigzag_worker_backward(gpu):
+    """The Zig-Zag worker (Q blocks 0 and 127 of a 512K sequence, 33 KV ranges of 16K)
+    forward + backward as the bench runs it: dQ on sampled rows of both Q blocks; dK and
+    dV at keys across the sequence with the upstream gradient kept on one query head."""
+    import torch
+    wl = W.config4(0)
+    dev = W.make_device_inputs(wl, seed=0)
+    pairs = build_pairs(wl)
+    o_part, lse_part = B.fcp_block_attn_fwd(dev["q"], dev["k"], dev["v"], pairs,
+                                            part_rows=int(pairs["q_len"].sum()))
+    o, lse = B.fcp_merge_partials(pairs, o_part, lse_part, wl.q_rows, wl.num_kv_heads)
+    del o_part, lse_part
+    dq, _, _ = B.fcp_block_attn_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], pairs)
+    torch.cuda.synchronize()
+    idx = oracle.SeqIndex(wl)
+    xr = {n: U.DeviceRows(dev[n]) for n in ("q", "k", "v", "do")}
+    rows = np.array([0, 1, 2047, 4095, 4096, 4097, 6000, 8191])
+    rq = oracle.dq_rows(xr["q"], xr["k"], xr["v"], xr["do"], idx, rows)
+    check_grad(dq.index_select(0, torch.as_tensor(rows, device=dq.device)).cpu().numpy(), rq,
+               "config4 dQ rows")
+    del dq
+    h0 = 50
+    g0 = h0 // (wl.num_q_heads // wl.num_kv_heads)
+    _, dk1, dv1 = B.fcp_block_attn_bwd(dev["q"], dev["k"], dev["v"], o, lse,
+                                       _one_head(dev["do"], h0), pairs)
+    torch.cuda.synchronize()
+    pos = [0, 1, 4095, 4096, 65536, 262143, 262144, 500000, 520191, 520192, 524287]
+    keys = np.array([int(idx.kv_row_of_pos[0][p]) for p in pos])
+    rk, rv = oracle.dkv_keys(xr["q"], xr["k"], xr["v"], xr["do"], idx, keys, heads=[h0])
+    kidx = torch.as_tensor(keys, device=dk1.device)
+    check_grad(dk1.index_select(0, kidx)[:, g0].cpu().numpy(), rk[:, g0], "config4 dK keys")
+    check_grad(dv1.index_select(0, kidx)[:, g0].cpu().numpy(), rv[:, g0], "config4 dV keys")

@@ -292,3 +292,38 @@ def test_dkv_rows_matches_full_backward(causal):
     sk, sv = oracle.dkv_rows(x["q"], x["k"], x["v"], x["do"], idx, rows)
     np.testing.assert_allclose(sk, dk[rows], atol=1e-13)
     np.testing.assert_allclose(sv, dv[rows], atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_dkv_keys_matches_full_backward(causal):
+    """dkv_keys (one forward per query, requested key columns only) against the full
+    backward, whose gradients are pinned by finite differences above; with a head subset
+    equal to one KV head's group, that KV head's rows are exact and the others zero."""
+    wl = W.custom([9, 14, 4], 5, 4, 2, 8, causal)
+    x = _inputs(wl)
+    idx = oracle.SeqIndex(wl)
+    _, dk, dv = oracle.backward(x["q"], x["k"], x["v"], x["do"], idx)
+    rows = np.array([26, 0, 4, 8, 9, 15, 22, 23])
+    sk, sv = oracle.dkv_keys(x["q"], x["k"], x["v"], x["do"], idx, rows)
+    np.testing.assert_allclose(sk, dk[rows], atol=1e-13)
+    np.testing.assert_allclose(sv, dv[rows], atol=1e-13)
+    hk, hv = oracle.dkv_keys(x["q"], x["k"], x["v"], x["do"], idx, rows, heads=[2, 3])
+    np.testing.assert_allclose(hk[:, 1], dk[rows, 1], atol=1e-13)
+    np.testing.assert_allclose(hv[:, 1], dv[rows, 1], atol=1e-13)
+    assert not hk[:, 0].any() and not hv[:, 0].any()
+
+
+def test_dkv_keys_single_head_equals_masked_upstream_gradient():
+    """Zeroing dO on every query head but one makes the other heads contribute nothing
+    (dS = P (dP - Delta) with dP = Delta = 0): the full backward with that dO equals
+    dkv_keys restricted to the one head."""
+    wl = W.custom([9, 14, 4], 5, 4, 2, 8, True)
+    x = _inputs(wl)
+    idx = oracle.SeqIndex(wl)
+    do1 = np.zeros_like(x["do"])
+    do1[:, 3] = x["do"][:, 3]
+    _, dk, dv = oracle.backward(x["q"], x["k"], x["v"], do1, idx)
+    rows = np.arange(wl.kv_rows)
+    hk, hv = oracle.dkv_keys(x["q"], x["k"], x["v"], x["do"], idx, rows, heads=[3])
+    np.testing.assert_allclose(hk, dk, atol=1e-13)
+    np.testing.assert_allclose(hv, dv, atol=1e-13)
