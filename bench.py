@@ -5,13 +5,16 @@ A step is one pass of the whole path over one batch: the host builds the block-p
 descriptors, the library plans and uploads its work lists, then the per-pair forward
 partials, the LSE merge, and the backward (Delta, dQ, dK/dV) run on the GPU. The metric
 is attention TFLOP/s (forward 4*D, backward 10*D per visible query-key pair and query
-head) and its fraction of the MI355X dense bf16 MFMA peak.
+head) and its fraction of the MI355X dense bf16 MFMA peak, against block size.
 
-Default workload: one worker's 16 x 1024-token share packed from lognormal lengths
-(median 4K, sigma 1.2), 64 query / 8 KV heads, head dim 128, causal. ``--sweep`` (on by
-default) adds the 32K single-sequence block-size sweep (512..4096, causal and
-non-causal, forward and forward+backward) as extra fields. Inputs are seeded synthetic
-bf16 N(0,1) data, resident in HBM before timing starts.
+Headline (``value``): forward + backward on one 32K-token causal sequence cut into
+4096-token blocks (every needed pair as a partial, then merged), 64 query / 8 KV heads,
+head dim 128. By default the run adds the block-size sweep (512 .. 16384, causal and
+non-causal: forward, fused forward, forward + backward, per-kernel rates and shader
+clock per row), the 1K-block worker share, the Zig-Zag worker of a 512K sequence and
+the heaviest worker of the heterogeneous lognormal batch (forward + backward), and the
+float64 oracle timed on the host cores. Inputs are seeded synthetic bf16 N(0,1) data,
+resident in HBM before timing starts.
 
 Prints one JSON line. ``--gpus`` above 1 is refused: the library runs on one GPU.
 """
@@ -33,12 +36,15 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--workload", default="config2", choices=["config2", "config3", "config4",
+    ap.add_argument("--workload", default="config3", choices=["config2", "config3", "config4",
                                                               "config5"])
     ap.add_argument("--block", type=int, default=4096, help="block size for config3")
+    ap.add_argument("--non-causal", action="store_true", help="non-causal mask for config3")
+    ap.add_argument("--no-legs", dest="legs", action="store_false", default=True,
+                    help="skip the 1K share, Zig-Zag and heterogeneous legs")
     ap.add_argument("--coalesce", type=int, default=None,
                     help="KV blocks coalesced per range for the Zig-Zag (default 4) and "
                          "heterogeneous (default 1) workloads")
@@ -128,7 +134,7 @@ def pipeline_bench(args):
         log("timing pipeline leg", name)
         ms[name], kt = timed(fn, args.steps, args.warmup, True)
         if "pipe_copy" in kt:
-            t, n = kt["pipe_copy"]
+            t, n = kt["pipe_copy"][:2]
             # bytes over the summed duration of the stages' copy batches
             copy_rate[name] = round(copy_bytes * args.steps / (t * 1e-3) / 1e9, 1)
     flops = W.fwd_flops(wl)
@@ -177,6 +183,7 @@ class Path:
         from block_wise_varlen_amd.descriptors import build_pairs, part_rows
         self.B, self.build_pairs, self.wl, self.dev, self.fused = B, build_pairs, wl, dev, fused
         pairs = build_pairs(wl)
+        self.pairs = pairs
         self.n_pairs = len(pairs)
         self.prow = part_rows(pairs)
         q, k = dev["q"], dev["k"]
@@ -219,15 +226,17 @@ class Path:
 
 
 def timed(fn, steps, warmup, kernel_times=False, per_step=None):
-    """Runs fn warmup + steps times; returns (ms per step, per-kernel {name: (ms, n)}).
-    With a list as per_step, also appends each timed step's own duration (events between
-    the steps, inside the same bracketed region)."""
+    """Runs fn warmup + steps times; returns (ms per step, per-kernel {name: (ms, n, MHz)}):
+    summed HIP-event time of each kernel's launches on the stream it ran on, their count,
+    and the average shader clock sampled inside the kernel (0 where not sampled). With a
+    list as per_step, also appends each timed step's own duration (events between the
+    steps, inside the same bracketed region)."""
     import torch
     from block_wise_varlen_amd import binding as B
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    B.fcp_timing_read()
+    B.fcp_timing_read_clock()
     if kernel_times:
         B.fcp_timing_enable(True)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
@@ -238,7 +247,7 @@ def timed(fn, steps, warmup, kernel_times=False, per_step=None):
             ev[i + 1].record()
     torch.cuda.synchronize()
     B.fcp_timing_enable(False)
-    kt = B.fcp_timing_read()
+    kt = B.fcp_timing_read_clock()
     if per_step is not None:
         per_step.extend(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     return ev[0].elapsed_time(ev[steps]) / steps, kt
@@ -302,9 +311,19 @@ def recorded_traffic(kernel, workload):
     return None
 
 
+def label(wl):
+    """Workload name with the knobs that change its pair table (block size and mask of
+    the 32K sweep, coalescing degree of the Zig-Zag and heterogeneous workers)."""
+    if wl.name.startswith("sweep-"):
+        return "%s/b%d-%s" % (wl.name, wl.block_size, "causal" if wl.causal else "noncausal")
+    if wl.coalesce and wl.coalesce > 1 or wl.name.startswith(("zigzag", "hetero")):
+        return "%s/c%d" % (wl.name, wl.coalesce or 1)
+    return wl.name
+
+
 def roofline(kt, steps, wl, pairs):
     name = max(kt, key=lambda n: kt[n][0])
-    total_ms, launches = kt[name]
+    total_ms, launches = kt[name][0], kt[name][1]
     avg_s = total_ms / launches / 1e3
     work, unit, bound = kernel_work(name, wl, pairs)
     if unit == "flop":
@@ -313,29 +332,41 @@ def roofline(kt, steps, wl, pairs):
         achieved, peak, u = work / avg_s / 1e9, PEAK_HBM_GBS, "GB/s"
     return {"bound": bound, "kernel": name, "achieved": round(achieved, 2), "peak": peak,
             "unit": u, "frac": round(achieved / peak, 4),
-            "traffic": recorded_traffic(name, wl.name),
+            "traffic": recorded_traffic(name, label(wl)),
             "avg_launch_ms": round(total_ms / launches, 4), "launches": launches}
 
 
 def kernel_rates(kt, wl, pairs):
-    """Achieved rate of every timed kernel against its own roofline: TFLOP/s of counted
-    work for the MFMA kernels, GB/s of algorithmic bytes for the HBM-bound ones."""
+    """Achieved rate of every timed kernel against its own roofline (TFLOP/s of counted
+    work for the MFMA kernels, GB/s of algorithmic bytes for the HBM-bound ones), its
+    average launch time, and the shader clock sampled inside it."""
     out = {}
-    for name, (total_ms, launches) in kt.items():
+    for name, rec in kt.items():
+        total_ms, launches = rec[0], rec[1]
+        mhz = rec[2] if len(rec) > 2 else 0.0
         try:
             work, unit, bound = kernel_work(name, wl, pairs)
         except (KeyError, ValueError):
             continue
-        if work is None:
-            continue
         avg_s = total_ms / launches / 1e3
-        if unit == "flop":
-            achieved, peak, u = work / avg_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
-        else:
-            achieved, peak, u = work / avg_s / 1e9, PEAK_HBM_GBS, "GB/s"
-        out[name] = {"achieved": round(achieved, 2), "unit": u, "frac": round(achieved / peak, 4),
-                     "bound": bound}
+        row = {"ms": round(total_ms / launches, 4), "bound": bound}
+        if work is not None:
+            if unit == "flop":
+                achieved, peak, u = work / avg_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+            else:
+                achieved, peak, u = work / avg_s / 1e9, PEAK_HBM_GBS, "GB/s"
+            row.update(achieved=round(achieved, 2), unit=u, frac=round(achieved / peak, 4))
+        if mhz:
+            row["sclk_mhz"] = round(mhz)
+        out[name] = row
     return out
+
+
+def leg_sclk(kt):
+    """Shader clock over a step: the kernels' sampled clocks weighted by their time."""
+    num = sum(r[0] * r[2] for r in kt.values() if len(r) > 2 and r[2])
+    den = sum(r[0] for r in kt.values() if len(r) > 2 and r[2])
+    return round(num / den) if den else None
 
 
 def calibration_copy(n_bytes=512 << 20, reps=3):
@@ -358,62 +389,160 @@ def calibration_copy(n_bytes=512 << 20, reps=3):
                                                  2 * n_bytes / ms / 1e6))
 
 
-def cpu_baseline(wl, seed):
-    """The float64 oracle (forward + backward) on one sequence of the same workload."""
+def measure(wl, dev, steps, warmup, forward_only=False, fused=False, per_step=None):
+    """One leg: (ms per step, kernel times) of the step on ``wl``, plus its summary."""
+    import fcp_workloads as W
+    path = Path(wl, dev, fused=fused)
+    ms, kt = timed(lambda: path.step(backward=not forward_only), steps, warmup, True,
+                   per_step=per_step)
+    fl = W.fwd_flops(wl) + (0 if forward_only else W.bwd_flops(wl))
+    tf = fl / ms / 1e9
+    summary = {"ms": round(ms, 3), "tflops": round(tf, 1),
+               "mfu": round(tf / PEAK_BF16_TFLOPS, 4), "sclk_mhz": leg_sclk(kt),
+               "kernel_rates": kernel_rates(kt, wl, path.pairs)}
+    return ms, kt, path.pairs, summary
+
+
+SWEEP_BLOCKS = (512, 1024, 2048, 4096, 8192, 16384)
+
+
+def sweep(base, steps=5, warmup=2):
+    """The 32K block-size sweep: per block size and mask, the forward (partials + merge),
+    the fused forward and forward + backward, each with per-kernel rates and clocks."""
+    import fcp_workloads as W
+    out = []
+    for causal in (True, False):
+        for b in SWEEP_BLOCKS:
+            wl = W.config3(b, causal)
+            _, _, pairs, f = measure(wl, base, steps, warmup, forward_only=True)
+            _, _, _, u = measure(wl, base, steps, warmup, forward_only=True, fused=True)
+            _, _, _, fb = measure(wl, base, steps, warmup)
+            row = {"block": b, "mask": "causal" if causal else "non-causal",
+                   "pairs": len(pairs),
+                   "fwd_ms": f["ms"], "fwd_tflops": f["tflops"], "fwd_mfu": f["mfu"],
+                   "fused_fwd_ms": u["ms"], "fused_fwd_tflops": u["tflops"],
+                   "fused_fwd_mfu": u["mfu"],
+                   "fwdbwd_ms": fb["ms"], "fwdbwd_tflops": fb["tflops"], "fwdbwd_mfu": fb["mfu"],
+                   "sclk_mhz": fb["sclk_mhz"], "kernel_rates": fb["kernel_rates"],
+                   "fwd_kernel_rates": f["kernel_rates"]}
+            log("sweep", json.dumps(row))
+            out.append(row)
+    return out
+
+
+def legs(seed, steps=3, warmup=1):
+    """Forward + backward on the other workers' shares: the 1K-block worker share, the
+    Zig-Zag worker (coalescing 4) and the heaviest heterogeneous worker (coalescing 1
+    and 4); also the fused-forward step on the share."""
+    import torch
+    import fcp_workloads as W
+    from fcp_workloads.tensors import host_to_device
+    out = {}
+    wl = W.config2(seed)
+    bits = W.make_host_inputs(wl, seed=seed)
+    dev = {n: host_to_device(b) for n, b in bits.items()}
+    for fused in (False, True):
+        _, _, pairs, r = measure(wl, dev, 10, 3, fused=fused)
+        r.update(workload=label(wl), pairs=len(pairs), seqlens=wl.seqlens,
+                 forward="fused" if fused else "partials+merge")
+        out["worker_1K_share" + ("_fused" if fused else "")] = r
+        log("leg", json.dumps(r))
+    del dev
+    for name, mk in (("zigzag_512K_c4", lambda: W.config4(0, coalesce=4)),
+                     ("hetero_c1", lambda: W.config5(seed, coalesce=1)),
+                     ("hetero_c4", lambda: W.config5(seed, coalesce=4))):
+        wl = mk()
+        torch.cuda.empty_cache()
+        dev = W.make_device_inputs(wl, seed=seed)
+        _, _, pairs, r = measure(wl, dev, steps, warmup)
+        _, _, _, f = measure(wl, dev, steps, warmup, forward_only=True)
+        r.update(workload=label(wl), pairs=len(pairs), q_rows=wl.q_rows, kv_rows=wl.kv_rows,
+                 fwd_ms=f["ms"], fwd_tflops=f["tflops"], fwd_mfu=f["mfu"])
+        out[name] = r
+        log("leg", json.dumps(r))
+        del dev
+    return out
+
+
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        return max(i["num_threads"] for i in info) if info else 1
+    except Exception:
+        return None
+
+
+def cpu_baseline(dev, seed):
+    """The float64 oracle (forward + backward, as it stands) on the host cores.
+
+    Headline sample: query head 0 (with KV head 0) of the headline workload -- all 32768
+    rows of the causal sequence, on the same bf16 values the GPU step read -- i.e. 1/64 of
+    its work. Also: the tiny three-sequence case in full and the 1K-block worker share's
+    3496-token sequence (all heads). The full headline and the Zig-Zag and heterogeneous
+    workers are extrapolated from the measured rate (labelled as such)."""
     import numpy as np
     import fcp_workloads as W
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max(i["num_threads"] for i in threadpool_info()) if threadpool_info() else 1
-    except Exception:
-        cores = os.cpu_count()
-    bits = W.make_host_inputs(wl, seed=seed)
-    x = {n: W.bf16_bits_to_f64(b) for n, b in bits.items()}
-    idx = oracle.SeqIndex(wl)
-    # the shortest sequence with at least 2048 tokens keeps the sample near 10-30 s
-    cands = [(L, s) for s, L in enumerate(wl.seqlens) if L >= 2048] or \
-        [(L, s) for s, L in enumerate(wl.seqlens)]
+
+    def f64(t):
+        import torch
+        return t.detach().cpu().view(torch.int16).numpy().view(np.uint16).astype(np.uint32) \
+            .__lshift__(16).view(np.float32).astype(np.float64)
+
+    def run(wl, x, seqs=None):
+        idx = oracle.SeqIndex(wl)
+        t0 = time.perf_counter()
+        oracle.forward(x["q"], x["k"], x["v"], idx)
+        oracle.backward(x["q"], x["k"], x["v"], x["do"], idx, seqs=seqs)
+        return time.perf_counter() - t0
+
+    def flops(wl, n_vis):
+        return 14 * wl.head_dim * wl.num_q_heads * n_vis
+
+    # headline sample: one query head and its KV head, as a 1-head workload of the same
+    # sequence (query head 0 reads KV head 0 in the 64/8 layout too)
+    head = W.config3(4096, True, hq=1, hkv=1)
+    x = {"q": f64(dev["q"][:, :1]), "k": f64(dev["k"][:, :1]), "v": f64(dev["v"][:, :1]),
+         "do": f64(dev["do"][:, :1])}
+    dt = run(head, x)
+    fl = flops(head, W.visible_pairs(head))
+    rate = fl / dt
+    tiny = W.config1()
+    bits = W.make_host_inputs(tiny, seed=seed)
+    dt1 = run(tiny, {n: W.bf16_bits_to_f64(b) for n, b in bits.items()})
+    share = W.config2(seed)
+    bits = W.make_host_inputs(share, seed=seed)
+    xs = {n: W.bf16_bits_to_f64(b) for n, b in bits.items()}
+    cands = [(L, s) for s, L in enumerate(share.seqlens) if L >= 2048] or \
+        [(L, s) for s, L in enumerate(share.seqlens)]
     length, s = min(cands)
+    idx = oracle.SeqIndex(share)
     t0 = time.perf_counter()
-    oracle.backward(x["q"], x["k"], x["v"], x["do"], idx, seqs=[s])
-    dt = time.perf_counter() - t0
-    n_vis = length * (length + 1) // 2 if wl.causal else length * length
-    flops = 14 * wl.head_dim * wl.num_q_heads * n_vis
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+    rows = np.nonzero(idx.q_row_seq == s)[0]
+    oracle.forward(xs["q"], xs["k"], xs["v"], idx, rows=rows)
+    oracle.backward(xs["q"], xs["k"], xs["v"], xs["do"], idx, seqs=[s])
+    dt2 = time.perf_counter() - t0
+    fl2 = flops(share, length * (length + 1) // 2)
+    extrap = {}
+    for name, wl in (("sweep_32K_b4096_causal", W.config3(4096, True)),
+                     ("sweep_32K_b4096_noncausal", W.config3(4096, False)),
+                     ("zigzag_512K", W.config4(0)), ("hetero_heaviest_worker", W.config5(seed))):
+        extrap[name] = round(flops(wl, W.visible_pairs(wl)) / rate, 1)
+    return {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": _threads(),
             "kind": "oracle", "seconds": round(dt, 2),
-            "sample": "float64 oracle forward+backward of sequence %d (%d tokens, all %d "
-                      "query heads) of the same workload, %.3g FLOP" % (s, length,
-                                                                       wl.num_q_heads, flops)}
-
-
-def sweep(seed, steps=5, warmup=2):
-    import fcp_workloads as W
-    out = []
-    base = W.make_device_inputs(W.config3(4096, True), seed=seed)
-    for causal in (True, False):
-        for b in (512, 1024, 2048, 4096):
-            wl = W.config3(b, causal)
-            path = Path(wl, base)
-            fl_f, fl_b = W.fwd_flops(wl), W.bwd_flops(wl)
-            ms_f, _ = timed(lambda: path.step(backward=False), steps, warmup)
-            ms_fb, kt = timed(lambda: path.step(backward=True), steps, warmup, True)
-            fused = Path(wl, base, fused=True)
-            ms_u, _ = timed(lambda: fused.step(backward=False), steps, warmup)
-            row = {"block": b, "mask": "causal" if causal else "non-causal",
-                   "pairs": path.n_pairs,
-                   "fwd_ms": round(ms_f, 3), "fwd_tflops": round(fl_f / ms_f / 1e9, 1),
-                   "fwd_mfu": round(fl_f / ms_f / 1e9 / PEAK_BF16_TFLOPS, 4),
-                   "fused_fwd_ms": round(ms_u, 3),
-                   "fused_fwd_tflops": round(fl_f / ms_u / 1e9, 1),
-                   "fwdbwd_ms": round(ms_fb, 3),
-                   "fwdbwd_tflops": round((fl_f + fl_b) / ms_fb / 1e9, 1),
-                   "fwdbwd_mfu": round((fl_f + fl_b) / ms_fb / 1e9 / PEAK_BF16_TFLOPS, 4),
-                   "kernel_ms": {k: round(v[0] / v[1], 4) for k, v in kt.items()}}
-            log("sweep", json.dumps(row))
-            out.append(row)
-            del path, fused
-    return out
+            "sample": "float64 oracle forward + backward of query head 0 (KV head 0) over all "
+                      "32768 rows of the headline workload (32K causal sequence), 1/64 of its "
+                      "work, %.3g FLOP" % fl,
+            "cpu_count": os.cpu_count(), "affinity_cores": len(os.sched_getaffinity(0)),
+            "blas_threads": _threads(),
+            "tiny_config_full": {"seconds": round(dt1, 3),
+                                 "tflops": round(flops(tiny, W.visible_pairs(tiny)) / dt1 / 1e12, 6)},
+            "worker_1K_share_sample": {"seconds": round(dt2, 2),
+                                       "tflops": round(fl2 / dt2 / 1e12, 6),
+                                       "sample": "sequence %d (%d tokens), all 64 query heads"
+                                                 % (s, length)},
+            "extrapolated_full_seconds": extrap}
 
 
 def main():
@@ -437,18 +566,17 @@ def main():
     import fcp_workloads as W
     from fcp_workloads.tensors import host_to_device
     from block_wise_varlen_amd import binding as B
-    from block_wise_varlen_amd.descriptors import build_pairs
     B.load()
     if not torch.cuda.is_available():
         print("no GPU available", file=sys.stderr)
         sys.exit(1)
 
     wl = {"config2": lambda: W.config2(args.seed),
-          "config3": lambda: W.config3(args.block, True),
+          "config3": lambda: W.config3(args.block, not args.non_causal),
           "config4": lambda: W.config4(0, coalesce=args.coalesce or 4),
           "config5": lambda: W.config5(args.seed, coalesce=args.coalesce or 1)}[args.workload]()
-    log("workload", wl.name, "q_rows", wl.q_rows, "kv_rows", wl.kv_rows)
-    if wl.rng == "host":
+    log("workload", label(wl), "q_rows", wl.q_rows, "kv_rows", wl.kv_rows)
+    if args.workload == "config2":
         bits = W.make_host_inputs(wl, seed=args.seed)
         dev = {n: host_to_device(b) for n, b in bits.items()}
         del bits
@@ -456,30 +584,29 @@ def main():
         dev = W.make_device_inputs(wl, seed=args.seed)
     if args.calibrate_copy:
         calibration_copy()
-    path = Path(wl, dev, fused=args.fused)
-    pairs = build_pairs(wl)
     fl_f, fl_b = W.fwd_flops(wl), W.bwd_flops(wl)
 
     log("timing fwd+merge")
-    ms_f, _ = timed(lambda: path.step(backward=False), args.steps, args.warmup)
+    ms_f, _, _, fwd = measure(wl, dev, args.steps, args.warmup, forward_only=True,
+                              fused=args.fused)
     log("timing full step (fwd + merge + bwd)")
     steps_ms = []
-    ms, kt = timed(lambda: path.step(backward=True), args.steps, args.warmup, True,
-                   per_step=steps_ms)
+    ms, kt, pairs, full = measure(wl, dev, args.steps, args.warmup, fused=args.fused,
+                                  per_step=steps_ms)
     steps_ms.sort()
     value = (fl_f + fl_b) / ms / 1e9
-    rl = roofline(kt, args.steps, wl, pairs)
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "block_size": wl.block_size, "tokens": wl.q_rows,
+        "config": {"workload": label(wl), "block_size": wl.block_size, "tokens": wl.q_rows,
                    "seqlens": wl.seqlens if len(wl.seqlens) <= 16 else len(wl.seqlens),
                    "heads_q": wl.num_q_heads, "heads_kv": wl.num_kv_heads,
                    "head_dim": wl.head_dim, "mask": "causal" if wl.causal else "non-causal",
                    "pairs": len(pairs), "coalesce": wl.coalesce, "seed": args.seed,
-                   "forward": "fused" if args.fused else "partials+merge"},
+                   "forward": "fused" if args.fused else "partials+merge",
+                   "step": "descriptors + forward + merge + backward (dQ, dK, dV)"},
         "mfu": round(value / PEAK_BF16_TFLOPS, 4),
         "fwd_tflops": round(fl_f / ms_f / 1e9, 2),
         "fwd_mfu": round(fl_f / ms_f / 1e9 / PEAK_BF16_TFLOPS, 4),
@@ -487,19 +614,25 @@ def main():
         "step_ms": {"median": round(steps_ms[len(steps_ms) // 2], 4),
                     "min": round(steps_ms[0], 4), "max": round(steps_ms[-1], 4)},
         "flops_per_step": fl_f + fl_b,
+        "sclk_mhz": full["sclk_mhz"],
         "kernel_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in kt.items()},
-        "roofline": rl,
-        "kernel_rates": kernel_rates(kt, wl, pairs),
+        "roofline": roofline(kt, args.steps, wl, pairs),
+        "kernel_rates": full["kernel_rates"],
+        "fwd_kernel_rates": fwd["kernel_rates"],
         "device": torch.cuda.get_device_name(0),
     }
     log(json.dumps(result))
-    if args.sweep:
-        del path
+    if args.sweep and args.workload == "config3":
         torch.cuda.empty_cache()
-        result["sweep"] = sweep(args.seed)
+        result["sweep"] = sweep(dev)
     if args.cpu:
         log("timing the oracle on the host")
-        result["cpu_baseline"] = cpu_baseline(wl, args.seed)
+        if args.workload == "config3" and args.block == 4096 and not args.non_causal:
+            result["cpu_baseline"] = cpu_baseline(dev, args.seed)
+    if args.legs and args.workload == "config3":
+        del dev
+        torch.cuda.empty_cache()
+        result["legs"] = legs(args.seed)
     print(json.dumps(result), flush=True)
 
 

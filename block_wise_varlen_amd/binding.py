@@ -25,7 +25,7 @@ SYMBOLS = ("fcp_abi_version", "fcp_status_string", "fcp_last_error", "fcp_valida
            "fcp_block_attn_fwd_fused", "fcp_block_attn_fwd_fused_noalloc",
            "fcp_block_attn_bwd", "fcp_timing_enable",
            "fcp_timing_read", "fcp_kernel_name", "fcp_comm_plan", "fcp_pipeline_fwd",
-           "fcp_pipeline_workspace_bytes", "fcp_plan_info")
+           "fcp_pipeline_workspace_bytes", "fcp_plan_info", "fcp_timing_read_clock")
 FCP_KERNEL_COUNT = 8
 FCP_PIPE_COPY_SHADER = 1
 
@@ -78,6 +78,7 @@ def load():
                                               P]),
         "fcp_timing_enable": (ctypes.c_int, [ctypes.c_int]),
         "fcp_timing_read": (ctypes.c_int, [P, P, I32]),
+        "fcp_timing_read_clock": (ctypes.c_int, [P, P, P, I32]),
         "fcp_kernel_name": (ctypes.c_char_p, [ctypes.c_int]),
         "fcp_comm_plan": (ctypes.c_int, [I32, I32, P, P, P, P]),
         "fcp_pipeline_fwd": (ctypes.c_int, [D, P, P, P, P, P, ctypes.c_int64, P, I32, P, P,
@@ -383,6 +384,19 @@ def fcp_timing_read():
     _check(load().fcp_timing_read(ctypes.cast(tot, ctypes.c_void_p),
                                   ctypes.cast(cnt, ctypes.c_void_p), FCP_KERNEL_COUNT))
     return {fcp_kernel_name(i): (tot[i], cnt[i]) for i in range(FCP_KERNEL_COUNT) if cnt[i]}
+
+
+def fcp_timing_read_clock():
+    """{kernel name: (total ms, launches, average shader clock in MHz or 0)} since the last
+    read (waits for the events)."""
+    tot = (ctypes.c_double * FCP_KERNEL_COUNT)()
+    cnt = (ctypes.c_int32 * FCP_KERNEL_COUNT)()
+    mhz = (ctypes.c_double * FCP_KERNEL_COUNT)()
+    _check(load().fcp_timing_read_clock(ctypes.cast(tot, ctypes.c_void_p),
+                                        ctypes.cast(cnt, ctypes.c_void_p),
+                                        ctypes.cast(mhz, ctypes.c_void_p), FCP_KERNEL_COUNT))
+    return {fcp_kernel_name(i): (tot[i], cnt[i], mhz[i]) for i in range(FCP_KERNEL_COUNT)
+            if cnt[i]}
 
 
 # ---- congestion-free communication plan (host only) --------------------------------

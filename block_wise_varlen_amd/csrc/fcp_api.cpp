@@ -173,6 +173,18 @@ hipError_t timed(int id, hipStream_t stream, F&& launch) {
   return err;
 }
 
+unsigned long long* clock_base();
+
+// Clock-sample slot of kernel `id` while timing is on (null otherwise).
+unsigned long long* clock_slot(int id) {
+  {
+    std::lock_guard<std::mutex> lk(g_time_mu);
+    if (!g_time_on) return nullptr;
+  }
+  unsigned long long* base = clock_base();
+  return base ? base + 2 * id : nullptr;
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int need_ptrs(std::initializer_list<const void*> ptrs) {
@@ -233,6 +245,26 @@ int scratch_address(void** out) {
   return FCP_OK;
 }
 
+// Shader-clock samples of timed launches (ClockStamp in the kernels): per kernel id, the
+// summed shader-clock and 100 MHz reference ticks of its workgroups, in a file-scope
+// device array whose per-device address is looked up like scratch's.
+__device__ __align__(256) unsigned long long clock_ticks[FCP_KERNEL_COUNT][2];
+void* g_clock_ptr[kMaxDevices] = {};
+
+// Address of this device's clock_ticks (zeroed when first looked up), or null.
+unsigned long long* clock_base() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_clock_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(clock_ticks)) != hipSuccess || !p) return nullptr;
+    if (hipMemset(p, 0, sizeof(clock_ticks)) != hipSuccess) return nullptr;
+    g_clock_ptr[dev] = p;
+  }
+  return static_cast<unsigned long long*>(g_clock_ptr[dev]);
+}
+
 template <class F>
 int guarded(F&& f) {
   try {
@@ -272,6 +304,10 @@ int fcp_timing_enable(int on) {
 }
 
 int fcp_timing_read(double* total_ms, int32_t* launches, int32_t n) {
+  return fcp_timing_read_clock(total_ms, launches, nullptr, n);
+}
+
+int fcp_timing_read_clock(double* total_ms, int32_t* launches, double* sclk_mhz, int32_t n) {
   return guarded([&] {
     std::vector<TimedLaunch> recs;
     {
@@ -294,10 +330,28 @@ int fcp_timing_read(double* total_ms, int32_t* launches, int32_t n) {
         if (launches) launches[r.id] += 1;
       }
     }
-    std::lock_guard<std::mutex> lk(g_time_mu);
-    for (const TimedLaunch& r : recs) {
-      g_time_free.push_back(r.begin);
-      g_time_free.push_back(r.end);
+    {
+      std::lock_guard<std::mutex> lk(g_time_mu);
+      for (const TimedLaunch& r : recs) {
+        g_time_free.push_back(r.begin);
+        g_time_free.push_back(r.end);
+      }
+    }
+    // Clock samples of this device's timed launches, all complete after the event waits.
+    for (int32_t i = 0; sclk_mhz && i < n; ++i) sclk_mhz[i] = 0.0;
+    int dev = 0;
+    void* cb = nullptr;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+      std::lock_guard<std::mutex> lk(g_scratch_mu);
+      cb = g_clock_ptr[dev];
+    }
+    if (cb) {
+      unsigned long long ticks[FCP_KERNEL_COUNT][2];
+      hipError_t e = hipMemcpy(ticks, cb, sizeof ticks, hipMemcpyDeviceToHost);
+      if (e == hipSuccess) e = hipMemset(cb, 0, sizeof ticks);
+      if (e != hipSuccess) return hip_err(e, "clock samples");
+      for (int32_t i = 0; sclk_mhz && i < n && i < FCP_KERNEL_COUNT; ++i)
+        if (ticks[i][1] > 0) sclk_mhz[i] = 100.0 * (double)ticks[i][0] / (double)ticks[i][1];
     }
     return st;
   });
@@ -381,6 +435,7 @@ int fcp_block_attn_fwd(const fcp_dims_t* dims, const void* q, const void* k, con
     a.scale_log2 = s.scale * 1.4426950408889634f;
     a.o_part = o_part;
     a.lse_part = lse_part;
+    a.clk = clock_slot(FCP_KERNEL_FWD);
     const hipError_t e =
         timed(FCP_KERNEL_FWD, stream, [&] { return fcp::launch_fwd(a, s.d, false, stream); });
     return e == hipSuccess ? FCP_OK : hip_err(e, "forward launch");
@@ -407,6 +462,7 @@ int fcp_block_attn_fwd_fused(const fcp_dims_t* dims, const void* q, const void* 
     a.scale_log2 = s.scale * 1.4426950408889634f;
     a.o = static_cast<uint16_t*>(o);
     a.lse = lse;
+    a.clk = clock_slot(FCP_KERNEL_FWD_FUSED);
     const hipError_t e = timed(FCP_KERNEL_FWD_FUSED, stream,
                                 [&] { return fcp::launch_fwd(a, s.d, true, stream); });
     return e == hipSuccess ? FCP_OK : hip_err(e, "fused forward launch");
@@ -516,9 +572,11 @@ int fcp_block_attn_bwd(const fcp_dims_t* dims, const void* q, const void* k, con
     a.part_dv = a.part_dk + part_floats;
     a.reduce = at<fcp::ReduceItem>(ws, P.off_reduce);
     a.n_reduce = P.n_reduce;
+    a.clk = clock_slot(FCP_KERNEL_DQ);
     hipError_t e =
         timed(FCP_KERNEL_DQ, stream, [&] { return fcp::launch_bwd_dq(a, s.d, stream); });
     if (e != hipSuccess) return hip_err(e, "dQ launch");
+    a.clk = clock_slot(FCP_KERNEL_DKDV);
     e = timed(FCP_KERNEL_DKDV, stream, [&] { return fcp::launch_bwd_dkdv(a, s.d, stream); });
     if (e != hipSuccess) return hip_err(e, "dK/dV launch");
     if (P.n_reduce > 0) {
@@ -633,6 +691,7 @@ int fcp_pipeline_fwd(const fcp_dims_t* dims, const void* q, void* k, void* v,
         a.scale_log2 = s.scale * 1.4426950408889634f;
         a.o_part = o_part;
         a.lse_part = lse_part;
+        a.clk = clock_slot(FCP_KERNEL_FWD);
         e = timed(FCP_KERNEL_FWD, stream, [&] { return fcp::launch_fwd(a, s.d, false, stream); });
         if (e != hipSuccess) break;
       }

@@ -46,6 +46,7 @@ template <int D, int CB>
 __global__ __launch_bounds__(64 * kColBlocksPerWG / CB)
 __attribute__((amdgpu_waves_per_eu(CB == 1 ? 2 : 1, CB == 1 ? 2 : 1)))
 void dq_kernel(BwdArgs a) {
+  const ClockStamp clock(a.clk);
   constexpr int NW = kColBlocksPerWG / CB;  // waves per workgroup
   constexpr int NKC = D / 16;
   constexpr int NDB = D / 32;
@@ -243,6 +244,7 @@ void dq_kernel(BwdArgs a) {
         *reinterpret_cast<f32x4_t*>(dst + d) = cur;
       }
   }
+  clock.done(a.clk);
 }
 
 // ---------------------------------------------------------------------------------
@@ -311,6 +313,9 @@ constexpr int kDkdvSplitRing = 6;
 template <int D>
 __global__ __launch_bounds__(64 * kDkdvSplitWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dkdv_split_kernel(BwdArgs a) {
+  // Thread 0 is a score wave's; it leaves after its last tile, when the gradient waves
+  // have only their final accumulation and stores left.
+  const ClockStamp clock(a.clk);
   constexpr int NKC = D / 16;
   constexpr int NDB = D / 32;
   constexpr int NW = kDkdvWaves;
@@ -434,6 +439,7 @@ void dkdv_split_kernel(BwdArgs a) {
       lds_barrier();
       cur = advance(cur);
     }
+    clock.done(a.clk);
     return;
   }
 

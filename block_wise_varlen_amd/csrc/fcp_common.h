@@ -259,4 +259,28 @@ __device__ __forceinline__ void wait_vmem_le() {
 }
 
 
+// Optional shader-clock sampling for measurement tools. With a non-null `clk`, thread 0
+// of each workgroup reads the shader-clock counter (s_memtime) and the 100 MHz reference
+// counter (s_memrealtime) when the workgroup starts and when it finishes, and adds the
+// two differences to clk[0] and clk[1]: their ratio over a launch is the average shader
+// clock in units of 100 MHz, weighted by workgroup lifetime. A null `clk` costs one
+// scalar branch at each end.
+struct ClockStamp {
+  uint64_t c0 = 0, r0 = 0;
+  __device__ explicit ClockStamp(unsigned long long* clk) {
+    if (clk && threadIdx.x == 0) {
+      c0 = __builtin_amdgcn_s_memtime();
+      r0 = __builtin_amdgcn_s_memrealtime();
+    }
+  }
+  __device__ void done(unsigned long long* clk) const {
+    if (clk && threadIdx.x == 0) {
+      const uint64_t c1 = __builtin_amdgcn_s_memtime();
+      const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+      atomicAdd(clk, (unsigned long long)(c1 - c0));
+      atomicAdd(clk + 1, (unsigned long long)(r1 - r0));
+    }
+  }
+};
+
 }  // namespace fcp

@@ -48,6 +48,7 @@ template <int D, bool FINAL, int CB>
 __global__ __launch_bounds__(64 * kColBlocksPerWG / CB)
 __attribute__((amdgpu_waves_per_eu(CB == 1 ? 2 : 1, CB == 1 ? 2 : 1)))
 void fwd_kernel(FwdArgs a) {
+  const ClockStamp clock(a.clk);
   constexpr int NW = kColBlocksPerWG / CB;  // waves per workgroup
   constexpr int NKC = D / 16;               // k-chunks of the QK^T contraction
   constexpr int NDB = D / 32;               // d-blocks of the output
@@ -370,6 +371,7 @@ void fwd_kernel(FwdArgs a) {
     if (seg_cur < seg_end) store(part_row0(seg_cur), false);
     for (int s2 = seg_cur + 1; s2 < seg_end; ++s2) store(part_row0(s2), true);
   }
+  clock.done(a.clk);
 }
 
 }  // namespace

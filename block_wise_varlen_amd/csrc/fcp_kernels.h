@@ -22,6 +22,7 @@ struct FwdArgs {
   float* lse_part;   // fp32 [part_rows, hq]
   uint16_t* o;       // bf16 [q_rows, hq, D]      (final mode)
   float* lse;        // fp32 [q_rows, hq]
+  unsigned long long* clk;  // optional clock sampling (ClockStamp), or null
 };
 
 struct MergeArgs {
@@ -59,6 +60,7 @@ struct BwdArgs {
   float* part_dv;
   const ReduceItem* reduce;
   int n_reduce;
+  unsigned long long* clk;  // optional clock sampling of the launched kernel, or null
 };
 
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool final_out, hipStream_t stream);

@@ -320,6 +320,17 @@ size_t fcp_pipeline_workspace_bytes(const fcp_dims_t* dims, const fcp_stage_t* s
 
 int fcp_timing_enable(int on);
 int fcp_timing_read(double* total_ms, int32_t* launches, int32_t n);
+
+/*
+ * fcp_timing_read, and in sclk_mhz[id] (n entries, or NULL) the average shader clock of
+ * the timed launches of kernel id on the calling thread's current device, in MHz (0 when
+ * none ran or the kernel takes no samples: the merge, the reduce and the copies). While
+ * timing is on, the forward, dQ and dK/dV kernels sample the shader-clock counter and a
+ * 100 MHz reference counter when each workgroup starts and ends; the value is the ratio
+ * of the summed differences times 100 MHz (a workgroup-lifetime-weighted average). The
+ * samples are reset by every read.
+ */
+int fcp_timing_read_clock(double* total_ms, int32_t* launches, double* sclk_mhz, int32_t n);
 const char* fcp_kernel_name(int id);
 
 /*

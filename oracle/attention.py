@@ -146,10 +146,12 @@ def merge(lses, outs):
     return out_o, out_lse
 
 
-def backward(qf, kf, vf, dof, idx, scale=None, seqs=None):
+def backward(qf, kf, vf, dof, idx, scale=None, seqs=None, heads=None):
     """Exact gradients of sum_i <dO_i, O_i> over the owned query rows of the chosen
-    sequences (all by default). Returns dQ [q_rows, Hq, D], dK and dV [kv_rows, Hkv, D]
-    (zeros outside those sequences)."""
+    sequences (all by default) and query heads (all by default; with a subset, dK and dV
+    sum over those heads only). Returns dQ [q_rows, Hq, D], dK and dV [kv_rows, Hkv, D]
+    (zeros outside those sequences and heads)."""
+    heads = list(range(idx.hq)) if heads is None else list(heads)
     group = idx.hq // idx.hkv
     sc = _scale(idx.d, scale)
     dq = np.zeros(qf.shape)
@@ -168,7 +170,7 @@ def backward(qf, kf, vf, dof, idx, scale=None, seqs=None):
         for a in range(0, len(r), step):
             rc, qp = r[a:a + step], pos[a:a + step]
             mask = (kpos[None, :] <= qp[:, None]) if idx.causal else None
-            for h in range(idx.hq):
+            for h in heads:
                 g = h // group
                 kk, vv = kf[krows, g], vf[krows, g]
                 smat = (qf[rc, h] @ kk.T) * sc

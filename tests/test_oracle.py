@@ -327,3 +327,17 @@ def test_dkv_keys_single_head_equals_masked_upstream_gradient():
     hk, hv = oracle.dkv_keys(x["q"], x["k"], x["v"], x["do"], idx, rows, heads=[3])
     np.testing.assert_allclose(hk, dk, atol=1e-13)
     np.testing.assert_allclose(hv, dv, atol=1e-13)
+
+
+def test_backward_head_subset_is_a_selection():
+    """backward(heads=...) returns the all-heads dQ on those heads (zero elsewhere), and
+    dK/dV of a KV head whose whole group is selected equal the all-heads result."""
+    wl = W.custom([9, 14, 4], 5, 4, 2, 8, True)
+    x = _inputs(wl)
+    idx = oracle.SeqIndex(wl)
+    dq, dk, dv = oracle.backward(x["q"], x["k"], x["v"], x["do"], idx)
+    sq, sk, sv = oracle.backward(x["q"], x["k"], x["v"], x["do"], idx, heads=[2, 3])
+    np.testing.assert_allclose(sq[:, 2:], dq[:, 2:], atol=1e-13)
+    assert not sq[:, :2].any() and not sk[:, 0].any() and not sv[:, 0].any()
+    np.testing.assert_allclose(sk[:, 1], dk[:, 1], atol=1e-13)
+    np.testing.assert_allclose(sv[:, 1], dv[:, 1], atol=1e-13)
