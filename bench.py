@@ -177,7 +177,7 @@ def comm_plan_bench(repeats=5):
 class Path:
     """Preallocated buffers and the step function for one workload."""
 
-    def __init__(self, wl, dev, fused=False):
+    def __init__(self, wl, dev, fused=False, part16=False):
         import torch
         from block_wise_varlen_amd import binding as B
         from block_wise_varlen_amd.descriptors import build_pairs, part_rows
@@ -189,7 +189,8 @@ class Path:
         q, k = dev["q"], dev["k"]
         hq, d = wl.num_q_heads, wl.head_dim
         f32 = torch.float32
-        self.o_part = None if fused else torch.empty((self.prow, hq, d), dtype=f32, device=q.device)
+        self.o_part = None if fused else torch.empty(
+            (self.prow, hq, d), dtype=torch.bfloat16 if part16 else f32, device=q.device)
         self.lse_part = None if fused else torch.empty((self.prow, hq), dtype=f32, device=q.device)
         self.o = torch.zeros_like(q)
         self.lse = torch.zeros((q.shape[0], hq), dtype=f32, device=q.device)
@@ -389,10 +390,12 @@ def calibration_copy(n_bytes=512 << 20, reps=3):
                                                  2 * n_bytes / ms / 1e6))
 
 
-def measure(wl, dev, steps, warmup, forward_only=False, fused=False, per_step=None):
-    """One leg: (ms per step, kernel times) of the step on ``wl``, plus its summary."""
+def measure(wl, dev, steps, warmup, forward_only=False, fused=False, per_step=None,
+            part16=False):
+    """One leg: (ms per step, kernel times) of the step on ``wl``, plus its summary.
+    ``part16``: the per-pair partials in bf16 (FCP_PART_BF16) instead of fp32."""
     import fcp_workloads as W
-    path = Path(wl, dev, fused=fused)
+    path = Path(wl, dev, fused=fused, part16=part16)
     ms, kt = timed(lambda: path.step(backward=not forward_only), steps, warmup, True,
                    per_step=per_step)
     fl = W.fwd_flops(wl) + (0 if forward_only else W.bwd_flops(wl))
@@ -407,19 +410,23 @@ SWEEP_BLOCKS = (512, 1024, 2048, 4096, 8192, 16384)
 
 
 def sweep(base, steps=5, warmup=2):
-    """The 32K block-size sweep: per block size and mask, the forward (partials + merge),
-    the fused forward and forward + backward, each with per-kernel rates and clocks."""
+    """The 32K block-size sweep: per block size and mask, the forward (fp32 partials +
+    merge, and bf16 partials + merge), the fused forward and forward + backward, each with
+    per-kernel rates and clocks."""
     import fcp_workloads as W
     out = []
     for causal in (True, False):
         for b in SWEEP_BLOCKS:
             wl = W.config3(b, causal)
             _, _, pairs, f = measure(wl, base, steps, warmup, forward_only=True)
+            _, _, _, h = measure(wl, base, steps, warmup, forward_only=True, part16=True)
             _, _, _, u = measure(wl, base, steps, warmup, forward_only=True, fused=True)
             _, _, _, fb = measure(wl, base, steps, warmup)
             row = {"block": b, "mask": "causal" if causal else "non-causal",
                    "pairs": len(pairs),
                    "fwd_ms": f["ms"], "fwd_tflops": f["tflops"], "fwd_mfu": f["mfu"],
+                   "fwd_bf16part_ms": h["ms"], "fwd_bf16part_tflops": h["tflops"],
+                   "fwd_bf16part_mfu": h["mfu"],
                    "fused_fwd_ms": u["ms"], "fused_fwd_tflops": u["tflops"],
                    "fused_fwd_mfu": u["mfu"],
                    "fwdbwd_ms": fb["ms"], "fwdbwd_tflops": fb["tflops"], "fwdbwd_mfu": fb["mfu"],

@@ -25,9 +25,12 @@ SYMBOLS = ("fcp_abi_version", "fcp_status_string", "fcp_last_error", "fcp_valida
            "fcp_block_attn_fwd_fused", "fcp_block_attn_fwd_fused_noalloc",
            "fcp_block_attn_bwd", "fcp_timing_enable",
            "fcp_timing_read", "fcp_kernel_name", "fcp_comm_plan", "fcp_pipeline_fwd",
-           "fcp_pipeline_workspace_bytes", "fcp_plan_info", "fcp_timing_read_clock")
+           "fcp_pipeline_workspace_bytes", "fcp_plan_info", "fcp_timing_read_clock",
+           "fcp_block_attn_fwd_ex", "fcp_merge_partials_ex")
 FCP_KERNEL_COUNT = 8
 FCP_PIPE_COPY_SHADER = 1
+FCP_PIPE_PART_BF16 = 2
+FCP_PART_F32, FCP_PART_BF16 = 0, 1
 
 
 class FcpError(RuntimeError):
@@ -72,6 +75,8 @@ def load():
         "fcp_workspace_bytes": (SZ, [D, P, I32, ctypes.c_int]),
         "fcp_block_attn_fwd": (ctypes.c_int, [D, P, P, P, P, I32, P, P, P, SZ, P]),
         "fcp_merge_partials": (ctypes.c_int, [D, P, I32, P, P, P, P, P, SZ, P]),
+        "fcp_block_attn_fwd_ex": (ctypes.c_int, [D, P, P, P, P, I32, P, P, I32, P, SZ, P]),
+        "fcp_merge_partials_ex": (ctypes.c_int, [D, P, I32, P, P, I32, P, P, P, SZ, P]),
         "fcp_block_attn_fwd_fused": (ctypes.c_int, [D, P, P, P, P, I32, P, P, P, SZ, P]),
         "fcp_block_attn_fwd_fused_noalloc": (ctypes.c_int, [D, P, P, P, P, I32, P, P, P]),
         "fcp_block_attn_bwd": (ctypes.c_int, [D, P, P, P, P, P, P, P, I32, P, P, P, P, SZ,
@@ -193,9 +198,20 @@ def fcp_plan_info(dims, pairs, op):
     return dict(zip(PLAN_INFO_FIELDS, (int(x) for x in out)))
 
 
+def _part_format(o_part):
+    import torch
+    if o_part.dtype == torch.float32:
+        return FCP_PART_F32
+    if o_part.dtype == torch.bfloat16:
+        return FCP_PART_BF16
+    raise TypeError("o_part must be float32 or bfloat16")
+
+
 def fcp_block_attn_fwd(q, k, v, pairs, o_part=None, lse_part=None, part_rows=None,
-                       softmax_scale=0.0, ws=None, stream=None):
-    """Per-pair partials. Returns (o_part fp32 [part_rows, Hq, D], lse_part fp32)."""
+                       softmax_scale=0.0, ws=None, stream=None, part_dtype=None):
+    """Per-pair partials. Returns (o_part [part_rows, Hq, D], lse_part fp32 [part_rows,
+    Hq]); o_part is fp32 (fcp_block_attn_fwd) or, with part_dtype=torch.bfloat16 or a
+    bf16 o_part, bf16 (fcp_block_attn_fwd_ex, FCP_PART_BF16)."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, torch.bfloat16, n)
@@ -204,28 +220,36 @@ def fcp_block_attn_fwd(q, k, v, pairs, o_part=None, lse_part=None, part_rows=Non
         part_rows = o_part.shape[0] if o_part is not None else \
             int((arr["out_row"] + arr["q_len"]).max()) if n else 0
     if o_part is None:
-        o_part = torch.empty((part_rows, q.shape[1], q.shape[2]), dtype=torch.float32,
-                             device=q.device)
+        o_part = torch.empty((part_rows, q.shape[1], q.shape[2]),
+                             dtype=part_dtype or torch.float32, device=q.device)
     if lse_part is None:
         lse_part = torch.empty((part_rows, q.shape[1]), dtype=torch.float32, device=q.device)
-    _need(o_part, torch.float32, "o_part")
+    fmt = _part_format(o_part)
+    _need(o_part, o_part.dtype, "o_part")
     _need(lse_part, torch.float32, "lse_part")
     dims = _dims_from(q, k, part_rows, softmax_scale)
     lib = load()
     ws, wsb = _workspace(lambda: lib.fcp_workspace_bytes(ctypes.byref(dims), p, n, FCP_OP_FWD),
                          q, ws, stream)
-    _check(lib.fcp_block_attn_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), p, n,
-                                  _ptr(o_part), _ptr(lse_part), _ptr(ws), wsb,
-                                  _stream(q, stream)))
+    if fmt == FCP_PART_F32:
+        _check(lib.fcp_block_attn_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), p, n,
+                                      _ptr(o_part), _ptr(lse_part), _ptr(ws), wsb,
+                                      _stream(q, stream)))
+    else:
+        _check(lib.fcp_block_attn_fwd_ex(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), p, n,
+                                         _ptr(o_part), _ptr(lse_part), fmt, _ptr(ws), wsb,
+                                         _stream(q, stream)))
     return o_part, lse_part
 
 
 def fcp_merge_partials(pairs, o_part, lse_part, q_rows, num_kv_heads=1, o=None, lse=None,
                        ws=None, stream=None):
-    """LSE merge into bf16 o [q_rows, Hq, D] and fp32 lse [q_rows, Hq]. Rows no pair
-    covers keep their previous contents (zeros when allocated here)."""
+    """LSE merge of fp32 or bf16 partials into bf16 o [q_rows, Hq, D] and fp32 lse
+    [q_rows, Hq]. Rows no pair covers keep their previous contents (zeros when allocated
+    here)."""
     import torch
-    _need(o_part, torch.float32, "o_part")
+    fmt = _part_format(o_part)
+    _need(o_part, o_part.dtype, "o_part")
     _need(lse_part, torch.float32, "lse_part")
     hq, d = o_part.shape[1], o_part.shape[2]
     if o is None:
@@ -240,8 +264,9 @@ def fcp_merge_partials(pairs, o_part, lse_part, q_rows, num_kv_heads=1, o=None, 
     ws, wsb = _workspace(
         lambda: lib.fcp_workspace_bytes(ctypes.byref(dims), p, n, FCP_OP_MERGE), o_part, ws,
         stream)
-    _check(lib.fcp_merge_partials(ctypes.byref(dims), p, n, _ptr(o_part), _ptr(lse_part),
-                                  _ptr(o), _ptr(lse), _ptr(ws), wsb, _stream(o_part, stream)))
+    _check(lib.fcp_merge_partials_ex(ctypes.byref(dims), p, n, _ptr(o_part), _ptr(lse_part),
+                                     fmt, _ptr(o), _ptr(lse), _ptr(ws), wsb,
+                                     _stream(o_part, stream)))
     return o, lse
 
 
@@ -339,7 +364,9 @@ def fcp_pipeline_fwd(q, k, v, k_src, v_src, stages, copies, pairs, o_part, lse_p
     import torch
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (k_src, "k_src"), (v_src, "v_src")):
         _need(t, torch.bfloat16, nm)
-    _need(o_part, torch.float32, "o_part")
+    if _part_format(o_part) == FCP_PART_BF16:
+        flags = int(flags) | FCP_PIPE_PART_BF16
+    _need(o_part, o_part.dtype, "o_part")
     _need(lse_part, torch.float32, "lse_part")
     if o is None:
         o = torch.zeros_like(q)

@@ -31,15 +31,74 @@ int hip_err(hipError_t e, const char* what) {
 }
 
 // Pinned host buffers used to upload work lists. A buffer is reused once the copy that
-// last read it has completed (its event has fired).
+// last read it has completed (its event has fired). The pool holds at most
+// kMaxStaging buffers: when every buffer is too small or still being read, an idle one is
+// replaced by a larger one, and when all of them are still being read the call waits
+// for the copy issued longest ago (only with more than kMaxStaging uploads in flight).
 struct Staging {
   void* ptr = nullptr;
   size_t bytes = 0;
   hipEvent_t ev = nullptr;
-  bool busy = false;
+  bool busy = false;      // a thread is between taking the buffer and recording its event
+  uint64_t last_use = 0;  // order of the last upload that read it
 };
+constexpr size_t kMaxStaging = 8;
 std::mutex g_pool_mu;
 std::vector<std::unique_ptr<Staging>> g_pool;
+uint64_t g_uploads = 0;
+
+// Under g_pool_mu: a buffer of at least n bytes whose last copy has completed, making room
+// or waiting as described above; null with *err set on a HIP failure.
+Staging* take_staging(size_t n, int* err) {
+  Staging* idle_small = nullptr;
+  Staging* oldest = nullptr;
+  for (auto& b : g_pool) {
+    if (b->busy) continue;
+    const bool idle = hipEventQuery(b->ev) == hipSuccess;
+    if (idle && b->bytes >= n) return b.get();
+    if (idle && (!idle_small || b->bytes < idle_small->bytes)) idle_small = b.get();
+    if (!oldest || b->last_use < oldest->last_use) oldest = b.get();
+  }
+  Staging* st = nullptr;
+  if (g_pool.size() < kMaxStaging) {
+    g_pool.push_back(std::make_unique<Staging>());
+    st = g_pool.back().get();
+    hipError_t e = hipEventCreateWithFlags(&st->ev, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      g_pool.pop_back();
+      *err = hip_err(e, "hipEventCreate(staging)");
+      return nullptr;
+    }
+  } else {
+    st = idle_small ? idle_small : oldest;
+    if (!st) {
+      *err = set_err(FCP_ERR_INTERNAL, "every staging buffer is in use by another thread");
+      return nullptr;
+    }
+    hipError_t e = hipEventSynchronize(st->ev);
+    if (e != hipSuccess) {
+      *err = hip_err(e, "staging event");
+      return nullptr;
+    }
+    if (st->bytes >= n) return st;
+    e = hipHostFree(st->ptr);
+    st->ptr = nullptr;
+    st->bytes = 0;
+    if (e != hipSuccess) {
+      *err = hip_err(e, "hipHostFree(staging)");
+      return nullptr;
+    }
+  }
+  const size_t bytes = n < (1u << 20) ? (1u << 20) : n;
+  hipError_t e = hipHostMalloc(&st->ptr, bytes, hipHostMallocDefault);
+  if (e != hipSuccess) {
+    st->ptr = nullptr;
+    *err = hip_err(e, "hipHostMalloc(staging)");
+    return nullptr;
+  }
+  st->bytes = bytes;
+  return st;
+}
 
 int upload(const std::vector<uint8_t>& blob, void* ws, hipStream_t stream) {
   const size_t n = blob.size();
@@ -47,23 +106,11 @@ int upload(const std::vector<uint8_t>& blob, void* ws, hipStream_t stream) {
   Staging* st = nullptr;
   {
     std::lock_guard<std::mutex> lk(g_pool_mu);
-    for (auto& b : g_pool) {
-      if (b->busy || b->bytes < n) continue;
-      if (hipEventQuery(b->ev) != hipSuccess) continue;
-      st = b.get();
-      break;
-    }
-    if (!st) {
-      auto b = std::make_unique<Staging>();
-      b->bytes = n < (1u << 20) ? (1u << 20) : n;
-      hipError_t e = hipHostMalloc(&b->ptr, b->bytes, hipHostMallocDefault);
-      if (e != hipSuccess) return hip_err(e, "hipHostMalloc(staging)");
-      e = hipEventCreateWithFlags(&b->ev, hipEventDisableTiming);
-      if (e != hipSuccess) return hip_err(e, "hipEventCreate(staging)");
-      st = b.get();
-      g_pool.push_back(std::move(b));
-    }
+    int err = FCP_OK;
+    st = take_staging(n, &err);
+    if (!st) return err;
     st->busy = true;
+    st->last_use = ++g_uploads;
   }
   std::memcpy(st->ptr, blob.data(), n);
   hipError_t e = hipMemcpyAsync(ws, st->ptr, n, hipMemcpyHostToDevice, stream);
@@ -417,7 +464,17 @@ size_t fcp_workspace_bytes(const fcp_dims_t* dims, const fcp_pair_t* pairs, int3
 int fcp_block_attn_fwd(const fcp_dims_t* dims, const void* q, const void* k, const void* v,
                        const fcp_pair_t* pairs, int32_t n_pairs, float* o_part,
                        float* lse_part, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return fcp_block_attn_fwd_ex(dims, q, k, v, pairs, n_pairs, o_part, lse_part, FCP_PART_F32,
+                               ws, ws_bytes, stream);
+}
+
+int fcp_block_attn_fwd_ex(const fcp_dims_t* dims, const void* q, const void* k, const void* v,
+                          const fcp_pair_t* pairs, int32_t n_pairs, void* o_part,
+                          float* lse_part, int32_t part_format, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
   return guarded([&] {
+    if (part_format != FCP_PART_F32 && part_format != FCP_PART_BF16)
+      return set_err(FCP_ERR_INVALID_ARG, "unknown partial format");
     fcp::Plan P;
     int st = prepare(dims, pairs, n_pairs, FCP_OP_FWD, {q, k, v, o_part, lse_part}, ws,
                      ws_bytes, stream, &P);
@@ -433,7 +490,10 @@ int fcp_block_attn_fwd(const fcp_dims_t* dims, const void* q, const void* k, con
     a.n_items = P.n_qitems;
     a.hq = s.hq, a.hkv = s.hkv, a.group = s.group, a.hpw = s.hpw, a.n_hgroups = s.n_hgroups;
     a.scale_log2 = s.scale * 1.4426950408889634f;
-    a.o_part = o_part;
+    if (part_format == FCP_PART_BF16)
+      a.o_part16 = static_cast<uint16_t*>(o_part);
+    else
+      a.o_part = static_cast<float*>(o_part);
     a.lse_part = lse_part;
     a.clk = clock_slot(FCP_KERNEL_FWD);
     const hipError_t e =
@@ -516,13 +576,25 @@ int fcp_block_attn_fwd_fused_noalloc(const fcp_dims_t* dims, const void* q, cons
 int fcp_merge_partials(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t n_pairs,
                        const float* o_part, const float* lse_part, void* o, float* lse,
                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  return fcp_merge_partials_ex(dims, pairs, n_pairs, o_part, lse_part, FCP_PART_F32, o, lse, ws,
+                               ws_bytes, stream);
+}
+
+int fcp_merge_partials_ex(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t n_pairs,
+                          const void* o_part, const float* lse_part, int32_t part_format,
+                          void* o, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
   return guarded([&] {
+    if (part_format != FCP_PART_F32 && part_format != FCP_PART_BF16)
+      return set_err(FCP_ERR_INVALID_ARG, "unknown partial format");
     fcp::Plan P;
     int st = prepare(dims, pairs, n_pairs, FCP_OP_MERGE, {o_part, lse_part, o, lse}, ws,
                      ws_bytes, stream, &P);
     if (st != FCP_OK || n_pairs == 0) return st;
     fcp::MergeArgs a{};
-    a.o_part = o_part;
+    if (part_format == FCP_PART_BF16)
+      a.o_part16 = static_cast<const uint16_t*>(o_part);
+    else
+      a.o_part = static_cast<const float*>(o_part);
     a.lse_part = lse_part;
     a.rows = at<fcp::RowItem>(ws, P.off_rows);
     a.parts = at<int32_t>(ws, P.off_parts);
@@ -611,7 +683,9 @@ int fcp_pipeline_fwd(const fcp_dims_t* dims, const void* q, void* k, void* v,
                      void* o, float* lse, int32_t flags, void* ws, size_t ws_bytes,
                      hipStream_t stream, hipStream_t copy_stream) {
   return guarded([&] {
-    if (flags & ~FCP_PIPE_COPY_SHADER) return set_err(FCP_ERR_INVALID_ARG, "unknown flag bits");
+    if (flags & ~(FCP_PIPE_COPY_SHADER | FCP_PIPE_PART_BF16))
+      return set_err(FCP_ERR_INVALID_ARG, "unknown flag bits");
+    const bool part16 = flags & FCP_PIPE_PART_BF16;
     fcp::PipelinePlan P;
     std::string msg;
     int st = fcp::make_pipeline_plan(dims, stages, n_stages, copies, pairs, depth, src_rows,
@@ -689,7 +763,10 @@ int fcp_pipeline_fwd(const fcp_dims_t* dims, const void* q, void* k, void* v,
         a.n_items = sp.n_qitems;
         a.hq = s.hq, a.hkv = s.hkv, a.group = s.group, a.hpw = s.hpw, a.n_hgroups = s.n_hgroups;
         a.scale_log2 = s.scale * 1.4426950408889634f;
-        a.o_part = o_part;
+        if (part16)
+          a.o_part16 = reinterpret_cast<uint16_t*>(o_part);
+        else
+          a.o_part = o_part;
         a.lse_part = lse_part;
         a.clk = clock_slot(FCP_KERNEL_FWD);
         e = timed(FCP_KERNEL_FWD, stream, [&] { return fcp::launch_fwd(a, s.d, false, stream); });
@@ -700,7 +777,10 @@ int fcp_pipeline_fwd(const fcp_dims_t* dims, const void* q, void* k, void* v,
     if (e == hipSuccess && P.n_pairs > 0) {
       void* base = static_cast<char*>(ws) + P.merge_off;
       fcp::MergeArgs a{};
-      a.o_part = o_part;
+      if (part16)
+        a.o_part16 = reinterpret_cast<const uint16_t*>(o_part);
+      else
+        a.o_part = o_part;
       a.lse_part = lse_part;
       a.rows = at<fcp::RowItem>(base, P.merge.off_rows);
       a.parts = at<int32_t>(base, P.merge.off_parts);

@@ -19,6 +19,7 @@
 
 #include <algorithm>
 #include <deque>
+#include <stdexcept>
 #include <vector>
 
 #include "fcp.h"

@@ -167,10 +167,11 @@ void fwd_kernel(FwdArgs a) {
           const float o1 = empty ? 0.f : acc[cb][db][4 * g4 + 1] * inv;
           const float o2 = empty ? 0.f : acc[cb][db][4 * g4 + 2] * inv;
           const float o3 = empty ? 0.f : acc[cb][db][4 * g4 + 3] * inv;
-          if constexpr (FINAL) {
+          if (FINAL || a.o_part16) {
+            // bf16 (RNE): the final output, or partials stored in bf16
             const uint32_t w0 = (uint32_t)f32_to_bf16(o0) | ((uint32_t)f32_to_bf16(o1) << 16);
             const uint32_t w1 = (uint32_t)f32_to_bf16(o2) | ((uint32_t)f32_to_bf16(o3) << 16);
-            *reinterpret_cast<u32x2_t*>(a.o + base + d) = u32x2_t{w0, w1};
+            *reinterpret_cast<u32x2_t*>((FINAL ? a.o : a.o_part16) + base + d) = u32x2_t{w0, w1};
           } else {
             *reinterpret_cast<f32x4_t*>(a.o_part + base + d) = f32x4_t{o0, o1, o2, o3};
           }
@@ -192,7 +193,7 @@ void fwd_kernel(FwdArgs a) {
 
   int buf = 0;
   bool first_tile = true;
-  // A store() issues 4 * NDB 16-byte stores per column block whose lane 0 holds a valid
+  // A store() issues 4 * NDB 16-byte (8-byte for bf16) stores per column block whose lane 0 holds a valid
   // row (the compiler skips the block only when no lane of the wave is valid), plus the
   // LSE store. kBurstStores counts the O stores of the wave's first column block: the
   // smallest number a store() of this wave issues, or 0 when it issues none.

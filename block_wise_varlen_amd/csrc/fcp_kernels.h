@@ -19,6 +19,7 @@ struct FwdArgs {
   int hq, hkv, group, hpw, n_hgroups;
   float scale_log2;  // softmax scale * log2(e)
   float* o_part;     // fp32 [part_rows, hq, D]   (per-pair mode)
+  uint16_t* o_part16;  // bf16 [part_rows, hq, D]  (per-pair mode, bf16 partials; else null)
   float* lse_part;   // fp32 [part_rows, hq]
   uint16_t* o;       // bf16 [q_rows, hq, D]      (final mode)
   float* lse;        // fp32 [q_rows, hq]
@@ -26,7 +27,8 @@ struct FwdArgs {
 };
 
 struct MergeArgs {
-  const float* o_part;
+  const float* o_part;      // fp32 partials, or
+  const uint16_t* o_part16;  // bf16 partials (non-null selects them)
   const float* lse_part;
   const RowItem* rows;
   const int32_t* parts;  // out_row of each partial, grouped per Q range

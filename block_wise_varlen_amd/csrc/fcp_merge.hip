@@ -14,7 +14,20 @@
 namespace fcp {
 namespace {
 
-template <int D>
+// Four consecutive partial values (element e4 of 4-value groups), from fp32 or bf16
+// partials.
+template <bool PB>
+__device__ __forceinline__ f32x4_t load4(const MergeArgs& a, int64_t e4) {
+  if constexpr (PB) {
+    const u32x2_t w = reinterpret_cast<const u32x2_t*>(a.o_part16)[e4];
+    return f32x4_t{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                   __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
+  } else {
+    return reinterpret_cast<const f32x4_t*>(a.o_part)[e4];
+  }
+}
+
+template <int D, bool PB>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   extern __shared__ float s_lse[];
   const RowItem it = a.rows[blockIdx.x];
@@ -53,7 +66,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
         for (int u = 0; u < 4; ++u) {
           const int64_t prow = parts[p + u] + it.row_in_group;
           w[u] = a.lse_part[prow * hq + h];
-          x[u] = reinterpret_cast<const f32x4_t*>(a.o_part)[prow * total + e];
+          x[u] = load4<PB>(a, prow * total + e);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) acc += __expf(w[u] - L) * x[u];
@@ -61,7 +74,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
       for (; p < np; ++p) {
         const int64_t prow = parts[p] + it.row_in_group;
         const float w = __expf(a.lse_part[prow * hq + h] - L);
-        acc += w * reinterpret_cast<const f32x4_t*>(a.o_part)[prow * total + e];
+        acc += w * load4<PB>(a, prow * total + e);
       }
     }
     const uint32_t w0 = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
@@ -75,10 +88,18 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream) {
   if (a.n_rows == 0) return hipSuccess;
   const size_t lds = (size_t)a.hq * sizeof(float);
-  if (head_dim == 128)
-    hipLaunchKernelGGL((merge_kernel<128>), dim3(a.n_rows), dim3(256), lds, stream, a);
-  else
-    hipLaunchKernelGGL((merge_kernel<64>), dim3(a.n_rows), dim3(256), lds, stream, a);
+  const bool pb = a.o_part16 != nullptr;
+  if (head_dim == 128) {
+    if (pb)
+      hipLaunchKernelGGL((merge_kernel<128, true>), dim3(a.n_rows), dim3(256), lds, stream, a);
+    else
+      hipLaunchKernelGGL((merge_kernel<128, false>), dim3(a.n_rows), dim3(256), lds, stream, a);
+  } else {
+    if (pb)
+      hipLaunchKernelGGL((merge_kernel<64, true>), dim3(a.n_rows), dim3(256), lds, stream, a);
+    else
+      hipLaunchKernelGGL((merge_kernel<64, false>), dim3(a.n_rows), dim3(256), lds, stream, a);
+  }
   return hipGetLastError();
 }
 

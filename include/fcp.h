@@ -32,8 +32,10 @@
  *  - `ws` is caller-owned device scratch of at least fcp_workspace_bytes(...) bytes for
  *    the same op and arguments; it must stay untouched until the stream passes the
  *    call. The library allocates no device memory; it owns only pinned host staging
- *    buffers used to upload its work lists, reused once their copies complete, and
- *    the 4 MiB static device array of fcp_block_attn_fwd_fused_noalloc.
+ *    buffers used to upload its work lists (at most 8, each reused once its copy has
+ *    completed; with more than 8 uploads still in flight a call waits for the oldest)
+ *    and two small static device arrays (the 4 MiB work-list array of
+ *    fcp_block_attn_fwd_fused_noalloc and the timing hook's clock samples).
  *  - Calls enqueue work on `stream` and return without waiting for it. They may be
  *    issued concurrently from several threads on distinct streams. Calls that share a
  *    workspace or output buffers must be ordered by the caller.
@@ -183,6 +185,22 @@ int fcp_block_attn_fwd(const fcp_dims_t* dims, const void* q, const void* k, con
                        float* lse_part, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Partial formats for the _ex variants. FCP_PART_F32: o_part is fp32, as above.
+ * FCP_PART_BF16: o_part holds the same normalised partial outputs rounded to bf16 (round
+ * to nearest even; [part_rows, num_q_heads, head_dim] 16-bit words), halving the bytes a
+ * pair writes and the merge reads; lse_part stays fp32. fcp_block_attn_fwd and
+ * fcp_merge_partials are the FCP_PART_F32 cases. An unknown format is
+ * FCP_ERR_INVALID_ARG.
+ */
+#define FCP_PART_F32 0
+#define FCP_PART_BF16 1
+
+int fcp_block_attn_fwd_ex(const fcp_dims_t* dims, const void* q, const void* k, const void* v,
+                          const fcp_pair_t* pairs, int32_t n_pairs, void* o_part,
+                          float* lse_part, int32_t part_format, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/*
  * LSE merge of partials (FCP paper Sec. 2.2: per-slice results reduce to the final
  * output). Pairs with identical (q_start, q_len) form a group; for every row and head
  * of a group, LSE = ln sum_i exp(LSE_i) and O = sum_i exp(LSE_i - LSE) O_i over the
@@ -193,6 +211,11 @@ int fcp_block_attn_fwd(const fcp_dims_t* dims, const void* q, const void* k, con
 int fcp_merge_partials(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t n_pairs,
                        const float* o_part, const float* lse_part, void* o, float* lse,
                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* fcp_merge_partials over partials in `part_format` (FCP_PART_F32 or FCP_PART_BF16). */
+int fcp_merge_partials_ex(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t n_pairs,
+                          const void* o_part, const float* lse_part, int32_t part_format,
+                          void* o, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Forward with the merge folded in: for every group of pairs with identical Q range,
@@ -262,7 +285,9 @@ int fcp_block_attn_bwd(const fcp_dims_t* dims, const void* q, const void* k, con
  * double buffering). The KV rows that stage s's copies write must not be read by the
  * pairs of stages s-R+1 .. s-1 (FCP_ERR_INVALID_ARG otherwise).
  * copy_stream == stream runs everything in order with no overlap. Copies use a DMA
- * engine (no compute units) unless flags has FCP_PIPE_COPY_SHADER (copy kernel).
+ * engine (no compute units) unless flags has FCP_PIPE_COPY_SHADER (copy kernel). With
+ * FCP_PIPE_PART_BF16 the partials in o_part are bf16 (FCP_PART_BF16 layout; o_part then
+ * points at part_rows * num_q_heads * head_dim 16-bit words).
  * k_src / v_src must not overlap k / v. Tables are host memory read during the call;
  * o_part / lse_part have dims->part_rows rows; all pairs together must satisfy the
  * checks of both FCP_OP_FWD and FCP_OP_MERGE. `ws` holds at least
@@ -280,6 +305,7 @@ typedef struct fcp_stage_t {
 } fcp_stage_t;
 
 #define FCP_PIPE_COPY_SHADER 1
+#define FCP_PIPE_PART_BF16 2
 
 int fcp_pipeline_fwd(const fcp_dims_t* dims, const void* q, void* k, void* v,
                      const void* k_src, const void* v_src, int64_t src_rows,

@@ -26,19 +26,29 @@ SMALL = {
 }
 
 
-def _run_partials(wl, dev, pairs):
+def _run_partials(wl, dev, pairs, part_dtype=None):
     o_part, lse_part = B.fcp_block_attn_fwd(dev["q"], dev["k"], dev["v"], pairs,
-                                            part_rows=part_rows(pairs))
+                                            part_rows=part_rows(pairs), part_dtype=part_dtype)
     return o_part, lse_part
 
 
+def _host(t):
+    import torch
+    return U.bf16_to_f64(t) if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+@pytest.mark.parametrize("part", ["f32", "bf16"])
 @pytest.mark.parametrize("name", list(SMALL))
-def test_partials_match_oracle(gpu, name):
+def test_partials_match_oracle(gpu, name, part):
+    """Every pair's partial (fp32, or bf16 with fp32 LSE) against the oracle's partial
+    over the pair's own keys, under the forward gates."""
+    import torch
     wl = SMALL[name]()
     dev, x = U.inputs(wl, seed=1)
     pairs = build_pairs(wl)
-    o_part, lse_part = _run_partials(wl, dev, pairs)
-    o_part, lse_part = o_part.cpu().numpy(), lse_part.cpu().numpy()
+    o_part, lse_part = _run_partials(wl, dev, pairs,
+                                     torch.bfloat16 if part == "bf16" else None)
+    o_part, lse_part = _host(o_part), lse_part.cpu().numpy()
     idx = oracle.SeqIndex(wl)
     kpos = U.kv_row_pos(wl)
     for i, p in enumerate(pairs):
@@ -65,6 +75,10 @@ def test_merge_and_fused_match_oracle(gpu, name):
     o_ref, l_ref = oracle.forward(x["q"], x["k"], x["v"], idx)
     U.check_attn(U.bf16_to_f64(o)[rows], lse.cpu().numpy()[rows], o_ref, l_ref, name + " merge")
     U.check_attn(U.bf16_to_f64(of)[rows], lf.cpu().numpy()[rows], o_ref, l_ref, name + " fused")
+    o_part16, lse_part16 = _run_partials(wl, dev, pairs, torch.bfloat16)
+    o16, l16 = B.fcp_merge_partials(pairs, o_part16, lse_part16, wl.q_rows, wl.num_kv_heads)
+    U.check_attn(U.bf16_to_f64(o16)[rows], l16.cpu().numpy()[rows], o_ref, l_ref,
+                 name + " merge of bf16 partials")
 
 
 def test_softmax_scale_and_constant_v(gpu):

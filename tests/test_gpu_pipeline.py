@@ -36,7 +36,7 @@ def packed(seed, causal, hq, hkv, d):
     return wl, local, {int(b): k for k, b in enumerate(order)}
 
 
-def run(wl, dev, P, overlap=True, flags=0, depth=None):
+def run(wl, dev, P, overlap=True, flags=0, depth=None, part_dtype=None):
     import torch
     shape = (P["kv_rows"], wl.num_kv_heads, wl.head_dim)
     k = torch.zeros(shape, dtype=torch.bfloat16, device=dev["q"].device)
@@ -45,8 +45,8 @@ def run(wl, dev, P, overlap=True, flags=0, depth=None):
         s, t, n = int(c["src_row"]), int(c["dst_row"]), int(c["n_rows"])
         k[t:t + n] = dev["k"][s:s + n]
         v[t:t + n] = dev["v"][s:s + n]
-    o_part = torch.empty((P["part_rows"], wl.num_q_heads, wl.head_dim), dtype=torch.float32,
-                         device=k.device)
+    o_part = torch.empty((P["part_rows"], wl.num_q_heads, wl.head_dim),
+                         dtype=part_dtype or torch.float32, device=k.device)
     lse_part = torch.empty((P["part_rows"], wl.num_q_heads), dtype=torch.float32,
                            device=k.device)
     cs = torch.cuda.Stream() if overlap else None
@@ -77,6 +77,21 @@ def test_pipeline_matches_oracle(gpu, name):
     rows = idx.owned_rows()
     o_ref, l_ref = oracle.forward(x["q"], x["k"], x["v"], idx)
     U.check_attn(U.bf16_to_f64(o)[rows], lse.cpu().numpy()[rows], o_ref, l_ref, name)
+
+
+@pytest.mark.parametrize("name", ["zigzag-N4-w0-c2", "packed-causal", "packed-noncausal-d64"])
+def test_pipeline_bf16_partials_match_oracle(gpu, name):
+    """The pipelined forward with its stage partials stored in bf16 (FCP_PIPE_PART_BF16)."""
+    import torch
+    wl, local, recv = CASES[name]()
+    dev, x = U.inputs(wl, seed=13, which=("q", "k", "v"))
+    P = build_pipeline(wl, local, recv, coalesce=wl.coalesce)
+    o, lse = run(wl, dev, P, part_dtype=torch.bfloat16)
+    idx = oracle.SeqIndex(wl)
+    rows = idx.owned_rows()
+    o_ref, l_ref = oracle.forward(x["q"], x["k"], x["v"], idx)
+    U.check_attn(U.bf16_to_f64(o)[rows], lse.cpu().numpy()[rows], o_ref, l_ref,
+                 name + " bf16 partials")
 
 
 @pytest.mark.parametrize("name", ["zigzag-N4-w0-c2", "packed-causal"])

@@ -1,7 +1,7 @@
 """GPU parity at every point of the 32K-token block-size sweep that bench.py reports
 (one sequence; blocks of 512 .. 16384 tokens; causal and non-causal), through the C ABI,
-in the bench's launch configuration: per-pair partials + LSE merge, and the fused
-forward, on sampled rows; the backward from the merged output on sampled dQ rows, with
+in the bench's launch configuration: per-pair partials (fp32, and bf16 with fp32 LSE) +
+LSE merge, and the fused forward, on sampled rows; the backward from the merged output on sampled dQ rows, with
 the per-sequence dV sum; and dK and dV element-wise at sampled keys, heavy ones at the
 start of the sequence (seen by nearly every query) and light ones at its end, in a
 second backward whose upstream gradient is kept on one query head (the other heads then
@@ -76,9 +76,16 @@ def test_sweep_point(inputs, block, causal):
                                             part_rows=part_rows(pairs))
     o, lse = B.fcp_merge_partials(pairs, o_part, lse_part, wl.q_rows, wl.num_kv_heads)
     del o_part, lse_part
+    o16, l16 = B.fcp_block_attn_fwd(dev["q"], dev["k"], dev["v"], pairs,
+                                    part_rows=part_rows(pairs), part_dtype=torch.bfloat16)
+    om, lm = B.fcp_merge_partials(pairs, o16, l16, wl.q_rows, wl.num_kv_heads)
+    del o16, l16
     of, lf = B.fcp_block_attn_fwd_fused(dev["q"], dev["k"], dev["v"], pairs)
     torch.cuda.synchronize()
     o_ref, l_ref = _ref("fwd", causal, x)
+    U.check_attn(U.bf16_to_f64(om.index_select(0, ridx)), lm.index_select(0, ridx).cpu().numpy(),
+                 o_ref, l_ref, name + " bf16 partials+merge")
+    del om, lm
     U.check_attn(U.bf16_to_f64(o.index_select(0, ridx)), lse.index_select(0, ridx).cpu().numpy(),
                  o_ref, l_ref, name + " partials+merge")
     U.check_attn(U.bf16_to_f64(of.index_select(0, ridx)), lf.index_select(0, ridx).cpu().numpy(),
