@@ -59,10 +59,24 @@ def _recorded(kernel, workload):
 
 
 def test_traffic_figure_is_dropped_when_the_kernel_sources_change(monkeypatch):
-    wl = W.config2(0)
-    rec = _recorded("bwd_dkdv", wl.name)
-    assert rec is not None, "no recorded traffic for the default workload's dominant kernel"
+    wl = W.config3(4096, True)   # the headline workload
+    name = bench.label(wl)
+    rec = _recorded("bwd_dkdv", name)
+    assert rec is not None, "no recorded traffic for the headline workload's dominant kernel"
     monkeypatch.setattr(bench, "sources_sha256", lambda: rec["sources_sha256"])
-    assert bench.recorded_traffic("bwd_dkdv", wl.name) == rec["bytes_per_launch"]
+    assert bench.recorded_traffic("bwd_dkdv", name) == rec["bytes_per_launch"]
     monkeypatch.setattr(bench, "sources_sha256", lambda: "0" * 64)
-    assert bench.recorded_traffic("bwd_dkdv", wl.name) is None
+    assert bench.recorded_traffic("bwd_dkdv", name) is None
+
+
+def test_labels_name_the_pair_table_knobs():
+    assert bench.label(W.config3(512, False)).endswith("/b512-noncausal")
+    assert bench.label(W.config3(4096, True)).endswith("/b4096-causal")
+    assert bench.label(W.config5(0, coalesce=4)).endswith("/c4")
+    assert bench.label(W.config2(0)) == W.config2(0).name
+
+
+def test_sclk_is_time_weighted_over_sampled_kernels():
+    kt = {"a": (10.0, 2, 2000.0), "b": (30.0, 2, 1800.0), "merge": (5.0, 2, 0.0)}
+    assert bench.leg_sclk(kt) == round((10 * 2000 + 30 * 1800) / 40)
+    assert bench.leg_sclk({"merge": (1.0, 1, 0.0)}) is None
