@@ -64,6 +64,11 @@ def load():
     if not os.path.exists(LIB_PATH):
         raise FileNotFoundError(
             "libfcp.so not built at %s (run python -m block_wise_varlen_amd.build)" % LIB_PATH)
+    # torch first: its HIP runtime (soname libamdhip64.so.7) is then the one libfcp.so
+    # binds to, so the process has a single runtime. Loaded the other way round, the
+    # library would bring in its own copy beside torch's, and the second runtime finds
+    # no device.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     D = ctypes.POINTER(FcpDims)
@@ -187,7 +192,8 @@ def fcp_workspace_bytes(dims, pairs, op):
 # ---- device entry points ----------------------------------------------------------
 
 PLAN_INFO_FIELDS = ("qitems", "kvitems", "split_tiles", "slots", "multihead_parts",
-                    "multihead_offset_parts", "ws_bytes")
+                    "multihead_offset_parts", "ws_bytes", "q_workgroups", "kv_workgroups",
+                    "empty_workgroups", "q_kvheads_per_xcd", "kv_kvheads_per_xcd")
 
 
 def fcp_plan_info(dims, pairs, op):

@@ -3,6 +3,7 @@
 // blocks on the stream; no exception crosses the ABI.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <exception>
@@ -433,6 +434,27 @@ int fcp_plan_info(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t n_pai
     v[FCP_PLAN_SPLIT_TILES] = P.n_reduce;
     v[FCP_PLAN_SLOTS] = P.n_slots;
     v[FCP_PLAN_WS_BYTES] = (int64_t)P.ws_bytes;
+    // Placement: launched workgroups, empty ones, and the most KV heads any XCD meets.
+    auto placement = [&](size_t off, int n, bool q_side, int64_t* most_heads) {
+      const fcp::WgMap* m = reinterpret_cast<const fcp::WgMap*>(P.blob.data() + off);
+      std::vector<std::vector<int>> heads(fcp::kXcds);
+      for (int b = 0; b < n; ++b) {
+        if (m[b].item < 0) {
+          ++v[FCP_PLAN_EMPTY_WORKGROUPS];
+          continue;
+        }
+        const int kvh = q_side ? m[b].head * P.shape.hpw / P.shape.group : m[b].head;
+        heads[b % fcp::kXcds].push_back(kvh);
+      }
+      for (auto& h : heads) {
+        std::sort(h.begin(), h.end());
+        *most_heads = std::max<int64_t>(*most_heads, std::unique(h.begin(), h.end()) - h.begin());
+      }
+    };
+    v[FCP_PLAN_Q_WORKGROUPS] = P.n_qwg;
+    v[FCP_PLAN_KV_WORKGROUPS] = P.n_kvwg;
+    if (P.n_qwg > 0) placement(P.off_qmap, P.n_qwg, true, &v[FCP_PLAN_Q_KVHEADS_PER_XCD]);
+    if (P.n_kvwg > 0) placement(P.off_kvmap, P.n_kvwg, false, &v[FCP_PLAN_KV_KVHEADS_PER_XCD]);
     if (P.n_kvitems > 0) {
       const fcp::KvItem* it = reinterpret_cast<const fcp::KvItem*>(P.blob.data() + P.off_kvitems);
       for (int i = 0; i < P.n_kvitems; ++i) {
@@ -485,6 +507,8 @@ int fcp_block_attn_fwd_ex(const fcp_dims_t* dims, const void* q, const void* k, 
     a.k = static_cast<const uint16_t*>(k);
     a.v = static_cast<const uint16_t*>(v);
     a.items = at<fcp::QItem>(ws, P.off_qitems);
+    a.wg = at<fcp::WgMap>(ws, P.off_qmap);
+    a.n_wg = P.n_qwg;
     a.segs = at<fcp::KvSeg>(ws, P.off_segs);
     a.seg_out = at<int32_t>(ws, P.off_segout);
     a.n_items = P.n_qitems;
@@ -516,6 +540,8 @@ int fcp_block_attn_fwd_fused(const fcp_dims_t* dims, const void* q, const void* 
     a.k = static_cast<const uint16_t*>(k);
     a.v = static_cast<const uint16_t*>(v);
     a.items = at<fcp::QItem>(ws, P.off_qitems);
+    a.wg = at<fcp::WgMap>(ws, P.off_qmap);
+    a.n_wg = P.n_qwg;
     a.segs = at<fcp::KvSeg>(ws, P.off_segs);
     a.n_items = P.n_qitems;
     a.hq = s.hq, a.hkv = s.hkv, a.group = s.group, a.hpw = s.hpw, a.n_hgroups = s.n_hgroups;
@@ -562,6 +588,8 @@ int fcp_block_attn_fwd_fused_noalloc(const fcp_dims_t* dims, const void* q, cons
     a.k = static_cast<const uint16_t*>(k);
     a.v = static_cast<const uint16_t*>(v);
     a.items = at<fcp::QItem>(ws, P.off_qitems);
+    a.wg = at<fcp::WgMap>(ws, P.off_qmap);
+    a.n_wg = P.n_qwg;
     a.segs = at<fcp::KvSeg>(ws, P.off_segs);
     a.n_items = P.n_qitems;
     a.hq = s.hq, a.hkv = s.hkv, a.group = s.group, a.hpw = s.hpw, a.n_hgroups = s.n_hgroups;
@@ -631,6 +659,10 @@ int fcp_block_attn_bwd(const fcp_dims_t* dims, const void* q, const void* k, con
     a.segs = at<fcp::KvSeg>(ws, P.off_segs);
     a.kvitems = at<fcp::KvItem>(ws, P.off_kvitems);
     a.qsegs = at<fcp::QSeg>(ws, P.off_qsegs);
+    a.qwg = at<fcp::WgMap>(ws, P.off_qmap);
+    a.kvwg = at<fcp::WgMap>(ws, P.off_kvmap);
+    a.n_qwg = P.n_qwg;
+    a.n_kvwg = P.n_kvwg;
     a.n_qitems = P.n_qitems;
     a.n_kvitems = P.n_kvitems;
     a.hq = s.hq, a.hkv = s.hkv, a.group = s.group, a.hpw = s.hpw, a.n_hgroups = s.n_hgroups;
@@ -758,6 +790,8 @@ int fcp_pipeline_fwd(const fcp_dims_t* dims, const void* q, void* k, void* v,
         a.k = static_cast<const uint16_t*>(k);
         a.v = static_cast<const uint16_t*>(v);
         a.items = at<fcp::QItem>(base, sp.off_qitems);
+        a.wg = at<fcp::WgMap>(base, sp.off_qmap);
+        a.n_wg = sp.n_qwg;
         a.segs = at<fcp::KvSeg>(base, sp.off_segs);
         a.seg_out = at<int32_t>(base, sp.off_segout);
         a.n_items = sp.n_qitems;

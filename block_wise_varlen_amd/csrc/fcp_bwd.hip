@@ -46,6 +46,8 @@ template <int D, int CB>
 __global__ __launch_bounds__(64 * kColBlocksPerWG / CB)
 __attribute__((amdgpu_waves_per_eu(CB == 1 ? 2 : 1, CB == 1 ? 2 : 1)))
 void dq_kernel(BwdArgs a) {
+  const WgMap wm = load_wg(a.qwg, blockIdx.x);
+  if (wm.item < 0) return;  // placement padding
   const ClockStamp clock(a.clk);
   constexpr int NW = kColBlocksPerWG / CB;  // waves per workgroup
   constexpr int NKC = D / 16;
@@ -53,9 +55,8 @@ void dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) u16 sK[kDqRing][kDqKt * D];
   __shared__ __attribute__((aligned(16))) u16 sV[kDqRing][kDqKt * D];
 
-  const int item_idx = blockIdx.x / a.n_hgroups;
-  const int hg = blockIdx.x - item_idx * a.n_hgroups;
-  const QItem it = a.qitems[item_idx];
+  const int hg = wm.head;
+  const QItem it = a.qitems[wm.item];
   const int head_base = hg * a.hpw;
   const int kvh = head_base / a.group;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -313,6 +314,8 @@ constexpr int kDkdvSplitRing = 6;
 template <int D>
 __global__ __launch_bounds__(64 * kDkdvSplitWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dkdv_split_kernel(BwdArgs a) {
+  const WgMap wm = load_wg(a.kvwg, blockIdx.x);
+  if (wm.item < 0) return;  // placement padding
   // Thread 0 is a score wave's; it leaves after its last tile, when the gradient waves
   // have only their final accumulation and stores left.
   const ClockStamp clock(a.clk);
@@ -329,9 +332,8 @@ void dkdv_split_kernel(BwdArgs a) {
   // gradient MFMAs; two slots, written in region t and read in region t + 1.
   __shared__ __attribute__((aligned(16))) bf16x8_t sX[2][NW][4][64];
 
-  const int item_idx = blockIdx.x / a.hkv;
-  const int kvh = blockIdx.x - item_idx * a.hkv;
-  const KvItem it = a.kvitems[item_idx];
+  const int kvh = wm.head;
+  const KvItem it = a.kvitems[wm.item];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pw = wave & (NW - 1);  // SIMD pair: keys pw * 32 .. + 31
@@ -597,8 +599,8 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(BwdArgs a) {
 constexpr int kDqCB = 1;
 
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t stream) {
-  if (a.n_qitems == 0) return hipSuccess;
-  const dim3 grid((unsigned)a.n_qitems * (unsigned)a.n_hgroups), block(64 * kColBlocksPerWG / kDqCB);
+  if (a.n_qwg == 0) return hipSuccess;
+  const dim3 grid((unsigned)a.n_qwg), block(64 * kColBlocksPerWG / kDqCB);
   if (head_dim == 128)
     hipLaunchKernelGGL((dq_kernel<128, kDqCB>), grid, block, 0, stream, a);
   else
@@ -607,8 +609,8 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t stream) {
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t stream) {
-  if (a.n_kvitems == 0) return hipSuccess;
-  const dim3 grid((unsigned)a.n_kvitems * (unsigned)a.hkv), block(64 * kDkdvSplitWaves);
+  if (a.n_kvwg == 0) return hipSuccess;
+  const dim3 grid((unsigned)a.n_kvwg), block(64 * kDkdvSplitWaves);
   if (head_dim == 128)
     hipLaunchKernelGGL((dkdv_split_kernel<128>), grid, block, 0, stream, a);
   else

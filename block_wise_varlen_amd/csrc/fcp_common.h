@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fcp_types.h"
+
 namespace fcp {
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
@@ -238,6 +240,13 @@ __device__ __forceinline__ T load_uniform(const T* table, int i) {
   const __attribute__((address_space(4))) u32x4_t* t =
       (const __attribute__((address_space(4))) u32x4_t*)table;
   return __builtin_bit_cast(T, t[__builtin_amdgcn_readfirstlane(i)]);
+}
+
+// Entry i of a workgroup launch map, through the scalar cache.
+__device__ __forceinline__ WgMap load_wg(const WgMap* map, int i) {
+  const __attribute__((address_space(4))) u32x2_t* t =
+      (const __attribute__((address_space(4))) u32x2_t*)map;
+  return __builtin_bit_cast(WgMap, t[__builtin_amdgcn_readfirstlane(i)]);
 }
 
 // Entry i of an int32 table, read through the scalar cache (a wave-uniform value).

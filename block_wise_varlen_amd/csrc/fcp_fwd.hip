@@ -48,6 +48,8 @@ template <int D, bool FINAL, int CB>
 __global__ __launch_bounds__(64 * kColBlocksPerWG / CB)
 __attribute__((amdgpu_waves_per_eu(CB == 1 ? 2 : 1, CB == 1 ? 2 : 1)))
 void fwd_kernel(FwdArgs a) {
+  const WgMap wm = load_wg(a.wg, blockIdx.x);
+  if (wm.item < 0) return;  // placement padding
   const ClockStamp clock(a.clk);
   constexpr int NW = kColBlocksPerWG / CB;  // waves per workgroup
   constexpr int NKC = D / 16;               // k-chunks of the QK^T contraction
@@ -56,9 +58,8 @@ void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) u16 sK[2][kFwdKt * D];
   __shared__ __attribute__((aligned(16))) u16 sV[2][kFwdKt * D];
 
-  const int item_idx = blockIdx.x / a.n_hgroups;
-  const int hg = blockIdx.x - item_idx * a.n_hgroups;
-  const QItem it = a.items[item_idx];
+  const int hg = wm.head;
+  const QItem it = a.items[wm.item];
   const int head_base = hg * a.hpw;
   const int kvh = head_base / a.group;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -385,8 +386,8 @@ void fwd_kernel(FwdArgs a) {
 constexpr int kFwdCB = FCP_FWD_CB;
 
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool final_out, hipStream_t stream) {
-  if (a.n_items == 0) return hipSuccess;
-  const dim3 grid((unsigned)a.n_items * (unsigned)a.n_hgroups), block(64 * kColBlocksPerWG / kFwdCB);
+  if (a.n_wg == 0) return hipSuccess;
+  const dim3 grid((unsigned)a.n_wg), block(64 * kColBlocksPerWG / kFwdCB);
   if (head_dim == 128) {
     if (final_out)
       hipLaunchKernelGGL((fwd_kernel<128, true, kFwdCB>), grid, block, 0, stream, a);

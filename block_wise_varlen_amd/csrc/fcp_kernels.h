@@ -12,7 +12,9 @@ struct FwdArgs {
   const uint16_t* q;   // bf16 [q_rows, hq, D]
   const uint16_t* k;   // bf16 [kv_rows, hkv, D]
   const uint16_t* v;   // bf16 [kv_rows, hkv, D]
-  const QItem* items;  // n_items, in launch order
+  const QItem* items;  // n_items
+  const WgMap* wg;     // launch order: workgroup -> (item, query-head group)
+  int n_wg;
   const KvSeg* segs;
   const int32_t* seg_out;  // per-pair mode: partial row of each KvSeg's first query
   int n_items;
@@ -51,6 +53,9 @@ struct BwdArgs {
   const KvSeg* segs;
   const KvItem* kvitems;
   const QSeg* qsegs;
+  const WgMap* qwg;   // dQ launch order: workgroup -> (item, query-head group)
+  const WgMap* kvwg;  // dK/dV launch order: workgroup -> (item, KV head)
+  int n_qwg, n_kvwg;
   int n_qitems, n_kvitems;
   int hq, hkv, group, hpw, n_hgroups;
   float scale;       // softmax scale

@@ -143,6 +143,65 @@ size_t put(std::vector<uint8_t>* blob, const std::vector<T>& v) {
   return off;
 }
 
+// One workgroup of a launch before placement: a work item with a head (query-head group
+// or KV head), its cost and the KV head whose K/V (forward, dQ) or Q tiles (dK/dV) it
+// reads.
+struct Unit {
+  int32_t item, head;
+  int64_t cost;
+  int32_t kv_head;
+};
+
+// Launch order that keeps the work of one KV head on its own XCDs, whose L2 then serves
+// the repeated reads of that head's K/V tiles (forward, dQ) or Q/dO tiles (dK/dV) (FCP
+// paper Sec. 3.1 ties the efficiency of small blocks to how often each loaded element is
+// reused). KV head h may use XCD x iff x % hkv == h % hkv when hkv divides kXcds (one
+// XCD per head at 8 heads, 8 / hkv XCDs per head below that), else x % kXcds ==
+// h % kXcds when kXcds divides hkv, else any XCD. Units go heaviest first, each to the
+// least-loaded XCD (by cost) it may use; the launch takes the XCDs' queues row by row,
+// one unit per XCD (workgroup b runs on XCD b % kXcds), with empty workgroups where a
+// queue runs out before the others. Measured: the earlier alternative of cutting each
+// head's Q ranges into contiguous per-XCD runs lost 15-21% at 2 and 1 KV heads (its XCDs
+// received unequal mixes of heavy and light items), and the order here keeps the
+// heaviest-first start that the 256 CUs need.
+std::vector<WgMap> xcd_order(std::vector<Unit> units, int hkv) {
+  std::stable_sort(units.begin(), units.end(),
+                   [](const Unit& a, const Unit& b) { return a.cost > b.cost; });
+  std::vector<std::vector<Unit>> queue(kXcds);
+  int64_t load[kXcds] = {};
+  for (const Unit& u : units) {
+    int best = -1;
+    for (int x = 0; x < kXcds; ++x) {
+      const bool ok = (kXcds % hkv == 0)   ? x % hkv == u.kv_head % hkv
+                      : (hkv % kXcds == 0) ? x == u.kv_head % kXcds
+                                           : true;
+      if (ok && (best < 0 || load[x] < load[best])) best = x;
+    }
+    queue[best].push_back(u);
+    load[best] += std::max<int64_t>(1, u.cost);
+  }
+  size_t rows = 0;
+  for (const auto& q : queue) rows = std::max(rows, q.size());
+  std::vector<WgMap> out;
+  out.reserve(rows * kXcds);
+  for (size_t j = 0; j < rows; ++j)
+    for (int x = 0; x < kXcds; ++x)
+      out.push_back(j < queue[x].size() ? WgMap{queue[x][j].item, queue[x][j].head}
+                                        : WgMap{-1, -1});
+  while (!out.empty() && out.back().item < 0) out.pop_back();
+  return out;
+}
+
+// Forward / dQ workgroups: every item for every query-head group.
+std::vector<WgMap> q_order(const std::vector<QItem>& items, const Shape& s) {
+  std::vector<Unit> units;
+  units.reserve(items.size() * s.n_hgroups);
+  for (int32_t i = 0; i < (int32_t)items.size(); ++i)
+    for (int32_t hg = 0; hg < s.n_hgroups; ++hg)
+      units.push_back(Unit{i, hg, items[i].cost, hg * s.hpw / s.group});
+  return xcd_order(std::move(units), s.hkv);
+}
+
 void sort_heaviest_first(std::vector<QItem>* items) {
   std::stable_sort(items->begin(), items->end(),
                    [](const QItem& a, const QItem& b) { return a.cost > b.cost; });
@@ -233,17 +292,23 @@ int make_plan(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t n_pairs, 
     std::vector<KvSeg> segs;
     std::vector<int32_t> seg_out;
     group_items(pairs, group_by_q(pairs, n_pairs), s, &items, &segs, &seg_out);
+    const std::vector<WgMap> qmap = q_order(items, s);
     P.off_qitems = put(&P.blob, items);
     P.off_segs = put(&P.blob, segs);
     P.off_segout = put(&P.blob, seg_out);
+    P.off_qmap = put(&P.blob, qmap);
     P.n_qitems = (int)items.size();
+    P.n_qwg = (int)qmap.size();
   } else if (op == FCP_OP_FWD_FUSED) {
     std::vector<QItem> items;
     std::vector<KvSeg> segs;
     group_items(pairs, group_by_q(pairs, n_pairs), s, &items, &segs);
+    const std::vector<WgMap> qmap = q_order(items, s);
     P.off_qitems = put(&P.blob, items);
     P.off_segs = put(&P.blob, segs);
+    P.off_qmap = put(&P.blob, qmap);
     P.n_qitems = (int)items.size();
+    P.n_qwg = (int)qmap.size();
   } else if (op == FCP_OP_MERGE) {
     std::vector<RowItem> rows;
     std::vector<int32_t> parts;
@@ -344,11 +409,22 @@ int make_plan(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t n_pairs, 
     kvitems.swap(split);
     std::stable_sort(kvitems.begin(), kvitems.end(),
                      [](const KvItem& x, const KvItem& y) { return x.cost > y.cost; });
+    // dK/dV workgroups: every item for every KV head.
+    std::vector<Unit> kunits;
+    kunits.reserve(kvitems.size() * s.hkv);
+    for (int32_t i = 0; i < (int32_t)kvitems.size(); ++i)
+      for (int32_t h = 0; h < s.hkv; ++h) kunits.push_back(Unit{i, h, kvitems[i].cost, h});
+    const std::vector<WgMap> kvmap = xcd_order(std::move(kunits), s.hkv);
+    const std::vector<WgMap> qmap = q_order(items, s);
     P.off_qitems = put(&P.blob, items);
     P.off_segs = put(&P.blob, segs);
     P.off_kvitems = put(&P.blob, kvitems);
     P.off_qsegs = put(&P.blob, qsegs);
     P.off_reduce = put(&P.blob, reduce);
+    P.off_qmap = put(&P.blob, qmap);
+    P.off_kvmap = put(&P.blob, kvmap);
+    P.n_qwg = (int)qmap.size();
+    P.n_kvwg = (int)kvmap.size();
     P.n_qitems = (int)items.size();
     P.n_kvitems = (int)kvitems.size();
     P.n_reduce = (int)reduce.size();

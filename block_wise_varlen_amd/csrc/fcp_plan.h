@@ -31,7 +31,9 @@ struct Plan {
   size_t ws_bytes = 0;        // blob + device-only regions
   size_t off_qitems = 0, off_segs = 0, off_rows = 0, off_parts = 0, off_segout = 0;
   size_t off_kvitems = 0, off_qsegs = 0, off_stats = 0, off_reduce = 0, off_partial = 0;
+  size_t off_qmap = 0, off_kvmap = 0;  // launch orders (WgMap) of the Q- and KV-side kernels
   int n_qitems = 0, n_rows = 0, n_kvitems = 0, n_reduce = 0, n_slots = 0;
+  int n_qwg = 0, n_kvwg = 0;           // workgroups (grid size) of those launches
 };
 
 // Validates dims and pairs for `op`; on failure returns the status and sets *err.

@@ -35,6 +35,20 @@ struct QItem {
   int32_t pad;
 };
 
+// XCDs of the target GPU. Workgroups of a launch are handed to the XCDs round robin in
+// workgroup-id order (workgroup b runs on XCD b % kXcds), so the launch order below
+// decides which XCD (and which of their separate L2 caches) a work item meets; only
+// locality, never correctness, depends on it.
+constexpr int kXcds = 8;
+
+// Workgroup b of a forward / dQ / dK/dV launch runs work item `item` for query-head group
+// (forward, dQ) or KV head (dK/dV) `head`; item < 0 marks an empty workgroup that exits
+// at once (padding that keeps the XCD assignment of the workgroups after it).
+struct WgMap {
+  int32_t item;
+  int32_t head;
+};
+
 // KV side of one pair as seen from its Q range.
 struct KvSeg {
   int32_t kv_start;     // first KV row

@@ -158,6 +158,16 @@ size_t fcp_workspace_bytes(const fcp_dims_t* dims, const fcp_pair_t* pairs,
  *   FCP_PLAN_MULTIHEAD_OFFSET_PARTS  of those, parts whose first head is not the first
  *                                    of the group
  *   FCP_PLAN_WS_BYTES                fcp_workspace_bytes() for the same arguments
+ *   FCP_PLAN_Q_WORKGROUPS            launched workgroups of the forward / dQ kernel
+ *   FCP_PLAN_KV_WORKGROUPS           launched workgroups of the dK/dV kernel (BWD)
+ *   FCP_PLAN_EMPTY_WORKGROUPS        of those, empty ones (placement padding)
+ *   FCP_PLAN_Q_KVHEADS_PER_XCD       the most distinct KV heads that the forward / dQ
+ *                                    workgroups placed on one XCD use
+ *   FCP_PLAN_KV_KVHEADS_PER_XCD      the same for the dK/dV workgroups
+ * Placement: workgroup b of a launch is taken to run on XCD b % 8 (round-robin dispatch
+ * over the 8 XCDs); the scheduler orders workgroups so that each KV head's work stays on
+ * its own XCDs (one XCD per head at 8 KV heads, 8 / num_kv_heads XCDs per head below
+ * that), heaviest first and balanced by cost. It affects locality only, never results.
  * Returns the status fcp_validate would return, or FCP_ERR_INVALID_ARG for a bad `out`.
  */
 #define FCP_PLAN_QITEMS 0
@@ -167,7 +177,12 @@ size_t fcp_workspace_bytes(const fcp_dims_t* dims, const fcp_pair_t* pairs,
 #define FCP_PLAN_MULTIHEAD_PARTS 4
 #define FCP_PLAN_MULTIHEAD_OFFSET_PARTS 5
 #define FCP_PLAN_WS_BYTES 6
-#define FCP_PLAN_INFO_COUNT 7
+#define FCP_PLAN_Q_WORKGROUPS 7
+#define FCP_PLAN_KV_WORKGROUPS 8
+#define FCP_PLAN_EMPTY_WORKGROUPS 9
+#define FCP_PLAN_Q_KVHEADS_PER_XCD 10
+#define FCP_PLAN_KV_KVHEADS_PER_XCD 11
+#define FCP_PLAN_INFO_COUNT 12
 
 int fcp_plan_info(const fcp_dims_t* dims, const fcp_pair_t* pairs, int32_t n_pairs, int op,
                   int64_t* out, int32_t n_out);

@@ -94,6 +94,24 @@ void check_plan(const fcp::Plan& P, int op, int n_pairs) {
     inside(P.off_qitems, P.n_qitems, sizeof(fcp::QItem));
     check(n_pairs == 0 || P.n_qitems > 0, "forward has items");
   }
+  // launch maps: every (item, head) exactly once, empty workgroups only as padding
+  auto check_map = [&](size_t off, int n_wg, int n_items, int n_heads) {
+    inside(off, n_wg, sizeof(fcp::WgMap));
+    if (n_wg == 0 || off + (size_t)n_wg * sizeof(fcp::WgMap) > blob) return;
+    const fcp::WgMap* m = reinterpret_cast<const fcp::WgMap*>(P.blob.data() + off);
+    std::vector<int> seen((size_t)n_items * n_heads, 0);
+    for (int b = 0; b < n_wg; ++b) {
+      if (m[b].item < 0) continue;
+      const bool ok = m[b].item < n_items && m[b].head >= 0 && m[b].head < n_heads;
+      check(ok, "map entry in range", m[b].item, m[b].head);
+      if (ok) ++seen[(size_t)m[b].item * n_heads + m[b].head];
+    }
+    for (size_t u = 0; u < seen.size(); ++u) check(seen[u] == 1, "unit launched once", (long long)u, seen[u]);
+    check(m[n_wg - 1].item >= 0, "no trailing empty workgroup");
+  };
+  if (op == FCP_OP_FWD || op == FCP_OP_FWD_FUSED || op == FCP_OP_BWD)
+    check_map(P.off_qmap, P.n_qwg, P.n_qitems, P.shape.n_hgroups);
+  if (op == FCP_OP_BWD) check_map(P.off_kvmap, P.n_kvwg, P.n_kvitems, P.shape.hkv);
   if (op == FCP_OP_MERGE) inside(P.off_rows, P.n_rows, sizeof(fcp::RowItem));
   if (op == FCP_OP_BWD) {
     inside(P.off_kvitems, P.n_kvitems, sizeof(fcp::KvItem));

@@ -183,3 +183,24 @@ def test_plan_info(lib):
     bad = B.make_dims(64, 7, 128, 10, 10)
     with pytest.raises(B.FcpError):
         B.fcp_plan_info(bad, pairs, B.FCP_OP_BWD)
+
+
+@pytest.mark.parametrize("hq,hkv,per_xcd", [(64, 8, 1), (16, 2, 1), (8, 1, 1), (128, 16, 2)])
+def test_xcd_placement(lib, hq, hkv, per_xcd):
+    """Workgroup b runs on XCD b % 8: the launch maps give each XCD as few KV heads as an
+    even split allows (one when there are at most 8), with padding only where runs differ
+    in length, and launch every unit once (checked in tests/sanitize)."""
+    wl = W.config3(4096, True, hq=hq, hkv=hkv)
+    pairs = build_pairs(wl)
+    dims = B.make_dims(hq, hkv, 128, wl.q_rows, wl.kv_rows)
+    for op in (B.FCP_OP_FWD_FUSED, B.FCP_OP_BWD):
+        info = B.fcp_plan_info(dims, pairs, op)
+        assert info["q_kvheads_per_xcd"] == per_xcd, info
+        real_q = info["qitems"] * (hq // min(8, hq // hkv))
+        assert info["q_workgroups"] >= real_q
+        if op == B.FCP_OP_BWD:
+            assert info["kv_kvheads_per_xcd"] == per_xcd, info
+            assert info["q_workgroups"] + info["kv_workgroups"] == \
+                real_q + info["kvitems"] * hkv + info["empty_workgroups"]
+        if hkv % 8 == 0:
+            assert info["empty_workgroups"] == 0
