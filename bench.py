@@ -628,6 +628,11 @@ def main():
         "fwd_kernel_rates": fwd["kernel_rates"],
         "device": torch.cuda.get_device_name(0),
     }
+    if not args.fused:
+        log("timing the full step with bf16 partials")
+        ms16, _, _, p16 = measure(wl, dev, args.steps, args.warmup, part16=True)
+        result["fwdbwd_bf16part"] = {"ms": p16["ms"], "tflops": p16["tflops"],
+                                     "mfu": p16["mfu"], "kernel_rates": p16["kernel_rates"]}
     log(json.dumps(result))
     if args.sweep and args.workload == "config3":
         torch.cuda.empty_cache()
