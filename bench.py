@@ -483,11 +483,13 @@ def _threads():
 def cpu_baseline(dev, seed):
     """The float64 oracle (forward + backward, as it stands) on the host cores.
 
-    Headline sample: query head 0 (with KV head 0) of the headline workload -- all 32768
-    rows of the causal sequence, on the same bf16 values the GPU step read -- i.e. 1/64 of
-    its work. Also: the tiny three-sequence case in full and the 1K-block worker share's
-    3496-token sequence (all heads). The full headline and the Zig-Zag and heterogeneous
-    workers are extrapolated from the measured rate (labelled as such)."""
+    Headline sample: query head 0 (with KV head 0) of the headline workload over its
+    first 23170 rows (their causal keys are the first 23170 positions, so this is exactly
+    that part of the headline's work: half of its visible pairs, 1/128 of the whole), on
+    the same bf16 values the GPU step read. Also: the tiny three-sequence case in full and
+    the 1K-block worker share's 3496-token sequence (all heads). The full headline and the
+    Zig-Zag and heterogeneous workers are extrapolated from the measured rate (labelled as
+    such)."""
     import numpy as np
     import fcp_workloads as W
     import oracle
@@ -507,11 +509,12 @@ def cpu_baseline(dev, seed):
     def flops(wl, n_vis):
         return 14 * wl.head_dim * wl.num_q_heads * n_vis
 
-    # headline sample: one query head and its KV head, as a 1-head workload of the same
-    # sequence (query head 0 reads KV head 0 in the 64/8 layout too)
-    head = W.config3(4096, True, hq=1, hkv=1)
-    x = {"q": f64(dev["q"][:, :1]), "k": f64(dev["k"][:, :1]), "v": f64(dev["v"][:, :1]),
-         "do": f64(dev["do"][:, :1])}
+    # headline sample: one query head and its KV head over the sequence's first rows, as
+    # a 1-head workload of that prefix (query head 0 reads KV head 0 in the 64/8 layout too)
+    n = 23170
+    head = W.custom([n], 4096, 1, 1, 128, True)
+    x = {"q": f64(dev["q"][:n, :1]), "k": f64(dev["k"][:n, :1]), "v": f64(dev["v"][:n, :1]),
+         "do": f64(dev["do"][:n, :1])}
     dt = run(head, x)
     fl = flops(head, W.visible_pairs(head))
     rate = fl / dt
@@ -538,9 +541,9 @@ def cpu_baseline(dev, seed):
         extrap[name] = round(flops(wl, W.visible_pairs(wl)) / rate, 1)
     return {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": _threads(),
             "kind": "oracle", "seconds": round(dt, 2),
-            "sample": "float64 oracle forward + backward of query head 0 (KV head 0) over all "
-                      "32768 rows of the headline workload (32K causal sequence), 1/64 of its "
-                      "work, %.3g FLOP" % fl,
+            "sample": "float64 oracle forward + backward of query head 0 (KV head 0) over the "
+                      "first 23170 rows of the headline workload (32K causal sequence): half of "
+                      "that head's visible pairs, 1/128 of the step's work, %.3g FLOP" % fl,
             "cpu_count": os.cpu_count(), "affinity_cores": len(os.sched_getaffinity(0)),
             "blas_threads": _threads(),
             "tiny_config_full": {"seconds": round(dt1, 3),
