@@ -312,6 +312,25 @@ def recorded_traffic(kernel, workload):
     return None
 
 
+def run_env():
+    """What the numbers were measured with: device architecture and CU count, HIP and
+    torch versions, the kernel sources' hash (the key of recorded traffic figures) and
+    the git revision when the tree has one."""
+    import subprocess
+    import torch
+    prop = torch.cuda.get_device_properties(0)
+    env = {"arch": getattr(prop, "gcnArchName", ""), "cus": prop.multi_processor_count,
+           "hip": torch.version.hip, "torch": torch.__version__,
+           "kernel_sources_sha256": sources_sha256()}
+    try:
+        env["git"] = subprocess.run(["git", "rev-parse", "--short=12", "HEAD"],
+                                    cwd=os.path.dirname(os.path.abspath(__file__)),
+                                    capture_output=True, text=True, timeout=10).stdout.strip() or None
+    except Exception:
+        env["git"] = None
+    return env
+
+
 def label(wl):
     """Workload name with the knobs that change its pair table (block size and mask of
     the 32K sweep, coalescing degree of the Zig-Zag and heterogeneous workers)."""
@@ -630,6 +649,7 @@ def main():
         "kernel_rates": full["kernel_rates"],
         "fwd_kernel_rates": fwd["kernel_rates"],
         "device": torch.cuda.get_device_name(0),
+        "env": run_env(),
     }
     if not args.fused:
         log("timing the full step with bf16 partials")
