@@ -174,6 +174,25 @@ def comm_plan_bench(repeats=5):
                                      "stages": k}}), flush=True)
 
 
+def covers_all(pairs, q_rows, kv_rows):
+    """True when the union of the pairs' Q ranges is [0, q_rows) and that of their KV
+    ranges is [0, kv_rows)."""
+    import numpy as np
+
+    def union_is(start, length, total):
+        if total == 0:
+            return True
+        mark = np.zeros(total + 1, dtype=np.int64)
+        np.add.at(mark, start, 1)
+        np.add.at(mark, start + length, -1)
+        return bool((np.cumsum(mark)[:total] > 0).all())
+
+    return (union_is(np.asarray(pairs["q_start"], np.int64), np.asarray(pairs["q_len"], np.int64),
+                     q_rows) and
+            union_is(np.asarray(pairs["kv_start"], np.int64),
+                     np.asarray(pairs["kv_len"], np.int64), kv_rows))
+
+
 class Path:
     """Preallocated buffers and the step function for one workload."""
 
@@ -202,6 +221,10 @@ class Path:
                    (B.FCP_OP_FWD, B.FCP_OP_MERGE, B.FCP_OP_BWD, B.FCP_OP_FWD_FUSED))
         # One workspace serves every call: the calls are ordered on one stream.
         self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        # When the pairs cover every Q row and every KV row, the backward writes the
+        # gradients (FCP_BWD_OVERWRITE: one writer per row) instead of adding them into
+        # zeroed buffers; otherwise the step zeroes them and accumulates.
+        self.overwrite = covers_all(pairs, q.shape[0], k.shape[0])
 
     def forward(self, pairs):
         B, x = self.B, self.dev
@@ -218,12 +241,14 @@ class Path:
         pairs = self.build_pairs(self.wl)
         self.forward(pairs)
         if backward:
-            self.dq.zero_()
-            self.dk.zero_()
-            self.dv.zero_()
+            if not self.overwrite:
+                self.dq.zero_()
+                self.dk.zero_()
+                self.dv.zero_()
             x = self.dev
             self.B.fcp_block_attn_bwd(x["q"], x["k"], x["v"], self.o, self.lse, x["do"], pairs,
-                                      dq=self.dq, dk=self.dk, dv=self.dv, ws=self.ws)
+                                      dq=self.dq, dk=self.dk, dv=self.dv, ws=self.ws,
+                                      overwrite=self.overwrite)
 
 
 def timed(fn, steps, warmup, kernel_times=False, per_step=None):
@@ -277,7 +302,7 @@ def kernel_work(name, wl, pairs):
 
 # Kernel sources whose hash a recorded HBM-traffic figure is tied to.
 KERNEL_SOURCES = ["fcp_common.h", "fcp_types.h", "fcp_kernels.h", "fcp_cursor.h",
-                  "fcp_fwd.hip", "fcp_bwd.hip", "fcp_merge.hip"]
+                  "fcp_fwd.hip", "fcp_bwd.hip", "fcp_bwd_dq.hip", "fcp_merge.hip"]
 
 
 def sources_sha256():
@@ -635,7 +660,9 @@ def main():
                    "head_dim": wl.head_dim, "mask": "causal" if wl.causal else "non-causal",
                    "pairs": len(pairs), "coalesce": wl.coalesce, "seed": args.seed,
                    "forward": "fused" if args.fused else "partials+merge",
-                   "step": "descriptors + forward + merge + backward (dQ, dK, dV)"},
+                   "step": "descriptors + forward + merge + backward (dQ, dK, dV)",
+                   "gradients": "written (FCP_BWD_OVERWRITE)" if covers_all(
+                       pairs, wl.q_rows, wl.kv_rows) else "zeroed, then added"},
         "mfu": round(value / PEAK_BF16_TFLOPS, 4),
         "fwd_tflops": round(fl_f / ms_f / 1e9, 2),
         "fwd_mfu": round(fl_f / ms_f / 1e9 / PEAK_BF16_TFLOPS, 4),

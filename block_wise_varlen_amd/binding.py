@@ -26,10 +26,11 @@ SYMBOLS = ("fcp_abi_version", "fcp_status_string", "fcp_last_error", "fcp_valida
            "fcp_block_attn_bwd", "fcp_timing_enable",
            "fcp_timing_read", "fcp_kernel_name", "fcp_comm_plan", "fcp_pipeline_fwd",
            "fcp_pipeline_workspace_bytes", "fcp_plan_info", "fcp_timing_read_clock",
-           "fcp_block_attn_fwd_ex", "fcp_merge_partials_ex")
+           "fcp_block_attn_fwd_ex", "fcp_merge_partials_ex", "fcp_block_attn_bwd_ex")
 FCP_KERNEL_COUNT = 8
 FCP_PIPE_COPY_SHADER = 1
 FCP_PIPE_PART_BF16 = 2
+FCP_BWD_OVERWRITE = 1
 FCP_PART_F32, FCP_PART_BF16 = 0, 1
 
 
@@ -86,6 +87,8 @@ def load():
         "fcp_block_attn_fwd_fused_noalloc": (ctypes.c_int, [D, P, P, P, P, I32, P, P, P]),
         "fcp_block_attn_bwd": (ctypes.c_int, [D, P, P, P, P, P, P, P, I32, P, P, P, P, SZ,
                                               P]),
+        "fcp_block_attn_bwd_ex": (ctypes.c_int, [D, P, P, P, P, P, P, P, I32, P, P, P, I32, P,
+                                                 SZ, P]),
         "fcp_timing_enable": (ctypes.c_int, [ctypes.c_int]),
         "fcp_timing_read": (ctypes.c_int, [P, P, I32]),
         "fcp_timing_read_clock": (ctypes.c_int, [P, P, P, I32]),
@@ -322,8 +325,10 @@ def fcp_block_attn_fwd_fused_noalloc(q, k, v, pairs, o=None, lse=None, softmax_s
 
 
 def fcp_block_attn_bwd(q, k, v, o, lse, dout, pairs, dq=None, dk=None, dv=None,
-                       softmax_scale=0.0, ws=None, stream=None):
-    """Adds gradients into fp32 dq, dk, dv (allocated zeroed here when not given)."""
+                       softmax_scale=0.0, ws=None, stream=None, overwrite=False):
+    """Adds gradients into fp32 dq, dk, dv (allocated zeroed here when not given); with
+    overwrite=True (fcp_block_attn_bwd_ex, FCP_BWD_OVERWRITE) writes them instead, in
+    the rows the pairs cover, leaving other rows as they were."""
     import torch
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
         _need(t, torch.bfloat16, nm)
@@ -341,9 +346,15 @@ def fcp_block_attn_bwd(q, k, v, o, lse, dout, pairs, dq=None, dk=None, dv=None,
     lib = load()
     ws, wsb = _workspace(lambda: lib.fcp_workspace_bytes(ctypes.byref(dims), p, n, FCP_OP_BWD),
                          q, ws, stream)
-    _check(lib.fcp_block_attn_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
-                                  _ptr(lse), _ptr(dout), p, n, _ptr(dq), _ptr(dk), _ptr(dv),
-                                  _ptr(ws), wsb, _stream(q, stream)))
+    if overwrite:
+        _check(lib.fcp_block_attn_bwd_ex(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                         _ptr(lse), _ptr(dout), p, n, _ptr(dq), _ptr(dk),
+                                         _ptr(dv), FCP_BWD_OVERWRITE, _ptr(ws), wsb,
+                                         _stream(q, stream)))
+    else:
+        _check(lib.fcp_block_attn_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                      _ptr(lse), _ptr(dout), p, n, _ptr(dq), _ptr(dk),
+                                      _ptr(dv), _ptr(ws), wsb, _stream(q, stream)))
     return dq, dk, dv
 
 

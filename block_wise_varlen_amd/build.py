@@ -26,6 +26,13 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags: the dQ kernel measured 1.6% faster with LLVM's max-ilp
+# scheduling strategy (the forward and dK/dV kernels were no faster with it).
+EXTRA_FLAGS = {
+    "fcp_bwd_dq.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith((".hip", ".cpp")))
@@ -33,9 +40,10 @@ def sources():
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
+    flags = FLAGS + EXTRA_FLAGS.get(os.path.basename(src), [])
+    cmd = [HIPCC] + flags + ["-c", src, "-o", obj]
     if src.endswith(".cpp"):
-        cmd = [HIPCC] + FLAGS + ["-x", "hip", "-c", src, "-o", obj]
+        cmd = [HIPCC] + flags + ["-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("compile failed: %s\n%s%s" % (" ".join(cmd), r.stdout, r.stderr))

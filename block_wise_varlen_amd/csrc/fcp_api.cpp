@@ -640,7 +640,17 @@ int fcp_block_attn_bwd(const fcp_dims_t* dims, const void* q, const void* k, con
                        const void* o, const float* lse, const void* dout,
                        const fcp_pair_t* pairs, int32_t n_pairs, float* dq, float* dk,
                        float* dv, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return fcp_block_attn_bwd_ex(dims, q, k, v, o, lse, dout, pairs, n_pairs, dq, dk, dv, 0, ws,
+                               ws_bytes, stream);
+}
+
+int fcp_block_attn_bwd_ex(const fcp_dims_t* dims, const void* q, const void* k, const void* v,
+                          const void* o, const float* lse, const void* dout,
+                          const fcp_pair_t* pairs, int32_t n_pairs, float* dq, float* dk,
+                          float* dv, int32_t flags, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
   return guarded([&] {
+    if (flags & ~FCP_BWD_OVERWRITE) return set_err(FCP_ERR_INVALID_ARG, "unknown flag bits");
     fcp::Plan P;
     int st = prepare(dims, pairs, n_pairs, FCP_OP_BWD, {q, k, v, o, lse, dout, dq, dk, dv}, ws,
                      ws_bytes, stream, &P);
@@ -671,6 +681,7 @@ int fcp_block_attn_bwd(const fcp_dims_t* dims, const void* q, const void* k, con
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
+    a.accumulate = (flags & FCP_BWD_OVERWRITE) ? 0 : 1;
     const size_t part_floats = (size_t)P.n_slots * s.hkv * fcp::kKvTileBwd * s.d;
     a.part_dk = reinterpret_cast<float*>(static_cast<char*>(ws) + P.off_partial);
     a.part_dv = a.part_dk + part_floats;

@@ -60,9 +60,10 @@ struct BwdArgs {
   int hq, hkv, group, hpw, n_hgroups;
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
-  float* dq;         // fp32 [q_rows, hq, D]   (+=)
-  float* dk;         // fp32 [kv_rows, hkv, D] (+=)
-  float* dv;         // fp32 [kv_rows, hkv, D] (+=)
+  float* dq;         // fp32 [q_rows, hq, D]   (+= when accumulate, else =)
+  float* dk;         // fp32 [kv_rows, hkv, D] (+= when accumulate, else =)
+  float* dv;         // fp32 [kv_rows, hkv, D] (+= when accumulate, else =)
+  int accumulate;    // 1: add into dq / dk / dv; 0: write them (each row has one writer)
   float* part_dk;    // fp32 [slots, hkv, kKvTileBwd, D] partials of split items
   float* part_dv;
   const ReduceItem* reduce;

@@ -278,6 +278,24 @@ int fcp_block_attn_bwd(const fcp_dims_t* dims, const void* q, const void* k, con
                        const fcp_pair_t* pairs, int32_t n_pairs, float* dq, float* dk,
                        float* dv, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* fcp_block_attn_bwd_ex flag: write the gradients instead of adding to them. */
+#define FCP_BWD_OVERWRITE 1
+
+/*
+ * fcp_block_attn_bwd with `flags`: 0 behaves exactly as fcp_block_attn_bwd; with
+ * FCP_BWD_OVERWRITE the rows of dq that some pair's Q range covers, and the rows of dk
+ * and dv that some pair's KV range covers, are WRITTEN with the gradient (every such row
+ * has exactly one writer, so the result equals zeroing them and adding), and every other
+ * row is left as it was. A caller that does not accumulate gradients across calls skips
+ * the zero-fill and the kernels' read of the old values. Other flag bits:
+ * FCP_ERR_INVALID_ARG.
+ */
+int fcp_block_attn_bwd_ex(const fcp_dims_t* dims, const void* q, const void* k, const void* v,
+                          const void* o, const float* lse, const void* dout,
+                          const fcp_pair_t* pairs, int32_t n_pairs, float* dq, float* dk,
+                          float* dv, int32_t flags, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
 /*
  * Block-level pipelined forward (FCP paper Sec. 4.2, "Block-level pipelining", Figure 7:
  * a worker's pull, compute and push are split into block-grained sub-stages that

@@ -80,3 +80,17 @@ def test_sclk_is_time_weighted_over_sampled_kernels():
     kt = {"a": (10.0, 2, 2000.0), "b": (30.0, 2, 1800.0), "merge": (5.0, 2, 0.0)}
     assert bench.leg_sclk(kt) == round((10 * 2000 + 30 * 1800) / 40)
     assert bench.leg_sclk({"merge": (1.0, 1, 0.0)}) is None
+
+
+def test_covers_all_decides_the_gradient_mode():
+    """The bench step writes the gradients (overwrite mode) only when the pairs' Q ranges
+    cover every Q row and their KV ranges every KV row."""
+    wl = W.config3(1024, True)
+    pairs = build_pairs(wl)
+    assert bench.covers_all(pairs, wl.q_rows, wl.kv_rows)
+    # Dropping the pairs of the last Q block leaves its rows uncovered.
+    last = pairs["q_start"] == pairs["q_start"].max()
+    assert not bench.covers_all(pairs[~last], wl.q_rows, wl.kv_rows)
+    # A KV row past every KV range is uncovered too.
+    assert not bench.covers_all(pairs, wl.q_rows, wl.kv_rows + 1)
+    assert bench.covers_all(pairs[:0], 0, 0)

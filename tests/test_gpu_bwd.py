@@ -4,6 +4,8 @@ Gate per gradient tensor (the pages give none; the arithmetic is bf16 products w
 accumulation, and the GPU's Delta uses the bf16-stored merged O): relative L2 <= 1e-2 and
 max-abs <= 5e-2 * max|reference|.
 """
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -69,6 +71,49 @@ def test_backward_accumulates_and_is_deterministic(gpu):
     for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
         torch.testing.assert_close(b, 2 * a, rtol=1e-6, atol=1e-6)
 
+
+
+@pytest.mark.parametrize("drop_last_q_range", [False, True])
+def test_overwrite_mode(gpu, drop_last_q_range):
+    """FCP_BWD_OVERWRITE writes the rows the pairs cover (bitwise what zeroing and adding
+    gives) and leaves every other row as it was; the workload's heavy key tiles are split
+    by heads, so the reduce kernel's write path runs too. With the last Q range's pairs
+    dropped, its Q rows (and any KV rows only those pairs read) stay untouched."""
+    import torch
+    wl = SMALL["g4-d128-ffd-coalesce"]()
+    dev, _ = U.inputs(wl, seed=9)
+    pairs = build_pairs(wl)
+    if drop_last_q_range:
+        pairs = pairs[pairs["q_start"] != pairs["q_start"].max()]
+    dims = B.make_dims(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.q_rows, wl.kv_rows)
+    assert B.fcp_plan_info(dims, pairs, B.FCP_OP_BWD)["slots"] > 0
+    o, lse = B.fcp_block_attn_fwd_fused(dev["q"], dev["k"], dev["v"], pairs)
+    ref = B.fcp_block_attn_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], pairs)
+    fill = 7.0
+    out = [torch.full(t.shape, fill, dtype=torch.float32, device=t.device) for t in ref]
+    B.fcp_block_attn_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], pairs, dq=out[0],
+                         dk=out[1], dv=out[2], overwrite=True)
+    torch.cuda.synchronize()
+    qcov = np.zeros(wl.q_rows, dtype=bool)
+    kcov = np.zeros(wl.kv_rows, dtype=bool)
+    for p in pairs:
+        qcov[p["q_start"]:p["q_start"] + p["q_len"]] = True
+        kcov[p["kv_start"]:p["kv_start"] + p["kv_len"]] = True
+    assert qcov.any() and kcov.any()
+    if drop_last_q_range:
+        assert not qcov.all()
+    for got, want, cov, name in ((out[0], ref[0], qcov, "dq"), (out[1], ref[1], kcov, "dk"),
+                                 (out[2], ref[2], kcov, "dv")):
+        c = torch.as_tensor(cov, device=got.device)
+        assert torch.equal(got[c], want[c]), name + ": covered rows differ"
+        assert bool((got[~c] == fill).all()), name + ": uncovered rows were written"
+    # Unknown flag bits are rejected before any work is enqueued.
+    _, pp, n = B._pairs_arg(pairs)
+    st = B.load().fcp_block_attn_bwd_ex(
+        ctypes.byref(dims), B._ptr(dev["q"]), B._ptr(dev["k"]), B._ptr(dev["v"]), B._ptr(o),
+        B._ptr(lse), B._ptr(dev["do"]), pp, n, B._ptr(out[0]), B._ptr(out[1]), B._ptr(out[2]),
+        2, None, 0, None)
+    assert st == 1  # FCP_ERR_INVALID_ARG
 
 def _key_sample(wl):
     rows = []
